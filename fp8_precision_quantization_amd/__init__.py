@@ -1,0 +1,18 @@
+"""libmxcast: bf16 -> MXFP8 casts and the 128x4 blocked e8m0 scale layout
+on AMD Instinct MI355X (gfx950), as hand-written HIP kernels behind a C ABI
+(include/mxcast.h).  This package is the thin Python binding over that ABI;
+the library is loaded on first use and its absence is an error."""
+from ._binding import (  # noqa: F401
+    MX_BLOCK,
+    MX_MAX_GROUPS,
+    MxError,
+    LIB_PATH,
+    lib,
+    mx_blocked_bytes,
+    mx_blocked_grouped_bytes,
+    mx_cast_dim0_dim1,
+    mx_cast_dim1_3d,
+    mx_scales_to_blocked,
+    mx_scales_to_blocked_grouped,
+    status_string,
+)

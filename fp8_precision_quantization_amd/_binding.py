@@ -1,0 +1,217 @@
+"""ctypes binding of libmxcast (include/mxcast.h).
+
+Argument marshalling only: shapes and dtypes are checked, outputs are
+allocated with torch (device memory is the only thing torch provides here),
+and every call goes to the C ABI on torch's current HIP stream.  There is no
+fallback: without the built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmxcast.so")
+
+MX_OK, MX_ERR_NULL, MX_ERR_SHAPE, MX_ERR_GROUPS, MX_ERR_HIP, MX_ERR_ALIGN = range(6)
+MX_BLOCK = 32
+MX_MAX_GROUPS = 1024
+
+_lib = None
+_lock = threading.Lock()
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+
+SIGNATURES = {
+    "mx_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "mx_cast_dim0_dim1": ([_vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
+    "mx_cast_dim1_3d": ([_vp, _i64, _i64, _i64, _vp, _vp, _vp], ctypes.c_int),
+    "mx_blocked_bytes": ([_i64, _i64, _i64], _i64),
+    "mx_scales_to_blocked": ([_vp, _i64, _i64, _i64, _vp, _vp], ctypes.c_int),
+    "mx_blocked_grouped_bytes": ([_i64, _i64, _i32, _i32], _i64),
+    "mx_scales_to_blocked_grouped": ([_vp, _i64, _i64, _vp, _i32, _i32, _vp, _vp, _vp],
+                                     ctypes.c_int),
+}
+
+
+class MxError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (where, status_string(status), status))
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(
+                    "libmxcast.so is missing at %s; build it with "
+                    "`python -m fp8_precision_quantization_amd.build`" % LIB_PATH)
+            handle = ctypes.CDLL(LIB_PATH)
+            for name, (args, res) in SIGNATURES.items():
+                f = getattr(handle, name)
+                f.argtypes = args
+                f.restype = res
+            _lib = handle
+        return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().mx_status_string(status).decode()
+
+
+def _check(status: int, where: str):
+    if status != MX_OK:
+        raise MxError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _as_u8(t):
+    return t if t.dtype == torch.uint8 else t.view(torch.uint8)
+
+
+def _out(t, shape, device, name):
+    if t is None:
+        return torch.empty(shape, dtype=torch.uint8, device=device)
+    t = _as_u8(t)
+    if tuple(t.shape) != tuple(shape) or not t.is_contiguous() or t.device != device:
+        raise ValueError("%s must be a contiguous %s tensor on %s" % (name, tuple(shape), device))
+    return t
+
+
+def _bf16_input(x, ndim, name):
+    if not isinstance(x, torch.Tensor) or not x.is_cuda:
+        raise ValueError("%s must be a CUDA (HIP) tensor" % name)
+    if x.dtype != torch.bfloat16:
+        raise ValueError("%s must be bfloat16, got %s" % (name, x.dtype))
+    if x.dim() != ndim:
+        raise ValueError("%s must have %d dimensions" % (name, ndim))
+    if not x.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _views(q, s, raw):
+    if raw:
+        return q, s
+    return q.view(torch.float8_e4m3fn), s.view(torch.float8_e8m0fnu)
+
+
+def mx_cast_dim0_dim1(x, dim0: bool = True, dim1: bool = True, out=None, raw: bool = False):
+    """bf16 (R, C) -> (q_row (R, C), s_row (R, C/32), q_col (C, R), s_col (C, R/32)).
+
+    q_col is the col-major cast stored as a row-major (C, R) array.  A
+    direction turned off returns None for its pair.  `out` may hold
+    preallocated uint8 outputs in the same order.  Results are e4m3 / e8m0
+    views unless raw=True (uint8)."""
+    _bf16_input(x, 2, "x")
+    rows, cols = x.shape
+    o = out if out is not None else (None, None, None, None)
+    q0 = _out(o[0], (rows, cols), x.device, "q_row") if dim0 else None
+    s0 = _out(o[1], (rows, cols // MX_BLOCK), x.device, "s_row") if dim0 else None
+    q1 = _out(o[2], (cols, rows), x.device, "q_col") if dim1 else None
+    s1 = _out(o[3], (cols, rows // MX_BLOCK), x.device, "s_col") if dim1 else None
+    _check(lib().mx_cast_dim0_dim1(_ptr(x), rows, cols, _ptr(q0), _ptr(s0), _ptr(q1), _ptr(s1),
+                                   _stream(x.device)), "mx_cast_dim0_dim1")
+    r0 = _views(q0, s0, raw) if dim0 else (None, None)
+    r1 = _views(q1, s1, raw) if dim1 else (None, None)
+    return r0[0], r0[1], r1[0], r1[1]
+
+
+def mx_cast_dim1_3d(w, out=None, raw: bool = False):
+    """bf16 (E, N, K) -> (q (E, K, N), s (E, K, N/32)), per-expert dim1 cast."""
+    _bf16_input(w, 3, "w")
+    e, n, k = w.shape
+    o = out if out is not None else (None, None)
+    q = _out(o[0], (e, k, n), w.device, "q")
+    s = _out(o[1], (e, k, n // MX_BLOCK), w.device, "s")
+    _check(lib().mx_cast_dim1_3d(_ptr(w), e, n, k, _ptr(q), _ptr(s), _stream(w.device)),
+           "mx_cast_dim1_3d")
+    return _views(q, s, raw)
+
+
+def mx_blocked_bytes(batch: int, rows: int, cols: int) -> int:
+    return lib().mx_blocked_bytes(batch, rows, cols)
+
+
+def mx_blocked_grouped_bytes(rows: int, cols: int, num_groups: int, group_axis: int) -> int:
+    return lib().mx_blocked_grouped_bytes(rows, cols, num_groups, group_axis)
+
+
+def _scale_input(s, name="scales"):
+    if not isinstance(s, torch.Tensor) or not s.is_cuda:
+        raise ValueError("%s must be a CUDA (HIP) tensor" % name)
+    s = _as_u8(s)
+    if not s.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return s
+
+
+def _pad(v, m):
+    return (v + m - 1) // m * m
+
+
+def mx_scales_to_blocked(s, out=None, raw: bool = False):
+    """e8m0 (R, C) or (B, R, C) -> blocked layout, shaped (ceil128(R), ceil4(C))
+    or (B, ceil128(R), ceil4(C)); every byte written."""
+    s = _scale_input(s)
+    if s.dim() == 2:
+        batch, (rows, cols) = 1, s.shape
+        shape = (_pad(rows, 128), _pad(cols, 4))
+    elif s.dim() == 3:
+        batch, rows, cols = s.shape
+        shape = (batch, _pad(rows, 128), _pad(cols, 4))
+    else:
+        raise ValueError("scales must be 2D or 3D")
+    o = _out(out, shape, s.device, "out")
+    _check(lib().mx_scales_to_blocked(_ptr(s), batch, rows, cols, _ptr(o), _stream(s.device)),
+           "mx_scales_to_blocked")
+    return o if raw else o.view(torch.float8_e8m0fnu)
+
+
+def mx_scales_to_blocked_grouped(s, group_end_offsets, group_axis: int, out=None,
+                                 out_group_starts=None, raw: bool = False):
+    """Grouped blocked layout with device-side END offsets (int32 [G]).
+
+    Returns (out, starts): out is (R + 128 G, ceil4(C)) for group_axis 0 and
+    (ceil128(R), ceil4(C) + 4 G) for group_axis 1; starts is int64 [G + 1] on
+    the device (padded start of each group, then the total)."""
+    s = _scale_input(s)
+    if s.dim() != 2:
+        raise ValueError("scales must be 2D")
+    offs = group_end_offsets
+    if not (isinstance(offs, torch.Tensor) and offs.is_cuda and offs.dtype == torch.int32
+            and offs.dim() == 1 and offs.is_contiguous()):
+        raise ValueError("group_end_offsets must be a contiguous int32 CUDA tensor")
+    rows, cols = s.shape
+    g = offs.numel()
+    if group_axis == 0:
+        shape = (rows + 128 * g, _pad(cols, 4))
+    elif group_axis == 1:
+        shape = (_pad(rows, 128), _pad(cols, 4) + 4 * g)
+    else:
+        raise ValueError("group_axis must be 0 or 1")
+    o = _out(out, shape, s.device, "out")
+    if out_group_starts is None:
+        starts = torch.empty(g + 1, dtype=torch.int64, device=s.device)
+    else:
+        starts = out_group_starts
+        if starts.dtype != torch.int64 or starts.numel() != g + 1 or not starts.is_contiguous():
+            raise ValueError("out_group_starts must be a contiguous int64 tensor of G + 1")
+    _check(lib().mx_scales_to_blocked_grouped(_ptr(s), rows, cols, _ptr(offs), g, group_axis,
+                                              _ptr(o), _ptr(starts), _stream(s.device)),
+           "mx_scales_to_blocked_grouped")
+    return (o if raw else o.view(torch.float8_e8m0fnu)), starts

@@ -1,0 +1,136 @@
+// C ABI of libmxcast: argument validation on the host, then one launch.
+// Every check runs before any HIP call, so a rejected call enqueues nothing
+// and the checks can be exercised on a machine without a GPU.
+#include <limits.h>
+
+#include "mx_launch.h"
+#include "mxcast.h"
+
+namespace {
+
+constexpr int64_t kMaxExtent = (int64_t)1 << 40;  // per-dimension bound, keeps products in int64
+constexpr int64_t kMaxGridBlocks = INT_MAX;
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+mx_status from_hip(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* mx_status_string(mx_status status) {
+  switch (status) {
+    case MX_OK: return "ok";
+    case MX_ERR_NULL: return "a required pointer is NULL";
+    case MX_ERR_SHAPE: return "unsupported shape (negative, not a multiple of 32, or too large)";
+    case MX_ERR_GROUPS: return "num_groups or group_axis out of range";
+    case MX_ERR_HIP: return "the HIP runtime rejected the launch";
+    case MX_ERR_ALIGN: return "a pointer is not aligned as required";
+  }
+  return "unknown status";
+}
+
+mx_status mx_cast_dim0_dim1(const void* x, int64_t rows, int64_t cols, uint8_t* q_row,
+                            uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, hipStream_t stream) {
+  if (rows < 0 || cols < 0 || rows % MX_BLOCK != 0 || cols % MX_BLOCK != 0 || rows > kMaxExtent ||
+      cols > kMaxExtent)
+    return MX_ERR_SHAPE;
+  if (rows == 0 || cols == 0)
+    return MX_OK;  // nothing to read or write; the pointers may be NULL
+  const bool d0 = q_row != nullptr || s_row != nullptr;
+  const bool d1 = q_col != nullptr || s_col != nullptr;
+  if (x == nullptr || (!d0 && !d1))
+    return MX_ERR_NULL;
+  if ((d0 && (q_row == nullptr || s_row == nullptr)) || (d1 && (q_col == nullptr || s_col == nullptr)))
+    return MX_ERR_NULL;
+  if (mx::cast_grid_blocks(rows, cols) > kMaxGridBlocks)
+    return MX_ERR_SHAPE;
+  if (!aligned(x, 16) || (d0 && !aligned(q_row, 8)) || (d1 && !aligned(q_col, 16)))
+    return MX_ERR_ALIGN;
+  return from_hip(mx::launch_cast_any(static_cast<const uint16_t*>(x), rows, cols, rows,
+                                      d0 ? q_row : nullptr, d0 ? s_row : nullptr,
+                                      d1 ? q_col : nullptr, d1 ? s_col : nullptr, stream));
+}
+
+mx_status mx_cast_dim1_3d(const void* w, int64_t experts, int64_t n, int64_t k, uint8_t* q,
+                          uint8_t* s, hipStream_t stream) {
+  if (experts < 0 || n < 0 || k < 0 || n % MX_BLOCK != 0 || k % MX_BLOCK != 0 ||
+      experts > kMaxExtent || n > kMaxExtent || k > kMaxExtent ||
+      (n > 0 && experts > kMaxExtent / n))
+    return MX_ERR_SHAPE;
+  if (experts == 0 || n == 0 || k == 0)
+    return MX_OK;  // nothing to read or write; the pointers may be NULL
+  if (w == nullptr || q == nullptr || s == nullptr)
+    return MX_ERR_NULL;
+  if (mx::cast_grid_blocks(experts * n, k) > kMaxGridBlocks)
+    return MX_ERR_SHAPE;
+  if (!aligned(w, 16) || !aligned(q, 16))
+    return MX_ERR_ALIGN;
+  return from_hip(mx::launch_cast_any(static_cast<const uint16_t*>(w), experts * n, k, n, nullptr,
+                                      nullptr, q, s, stream));
+}
+
+int64_t mx_blocked_bytes(int64_t batch, int64_t rows, int64_t cols) {
+  if (batch < 0 || rows < 0 || cols < 0 || batch > kMaxExtent || rows > kMaxExtent ||
+      cols > kMaxExtent)
+    return -1;
+  const int64_t per = round_up(rows, 128) * round_up(cols, 4);
+  if (per > 0 && batch > INT64_MAX / per)
+    return -1;
+  return batch * per;
+}
+
+mx_status mx_scales_to_blocked(const uint8_t* s, int64_t batch, int64_t rows, int64_t cols,
+                               uint8_t* out, hipStream_t stream) {
+  const int64_t bytes = mx_blocked_bytes(batch, rows, cols);
+  if (bytes < 0)
+    return MX_ERR_SHAPE;
+  if (bytes == 0)
+    return MX_OK;
+  if (out == nullptr || (s == nullptr && rows * cols > 0))
+    return MX_ERR_NULL;
+  if ((round_up(rows, 128) / 128) * batch * ((round_up(cols, 4) / 4 + 15) / 16) > kMaxGridBlocks)
+    return MX_ERR_SHAPE;
+  if (!aligned(out, 16))
+    return MX_ERR_ALIGN;
+  return from_hip(mx::launch_blocked_batched(s, batch, rows, cols, out, stream));
+}
+
+int64_t mx_blocked_grouped_bytes(int64_t rows, int64_t cols, int32_t num_groups,
+                                 int32_t group_axis) {
+  if (rows < 0 || cols < 0 || num_groups < 1 || num_groups > MX_MAX_GROUPS ||
+      (group_axis != 0 && group_axis != 1))
+    return -1;
+  if (rows + 128 * (int64_t)num_groups >= INT_MAX || cols + 4 * (int64_t)num_groups >= INT_MAX)
+    return -1;
+  if (group_axis == 0)
+    return (rows + 128 * (int64_t)num_groups) * round_up(cols, 4);
+  return round_up(rows, 128) * (round_up(cols, 4) + 4 * (int64_t)num_groups);
+}
+
+mx_status mx_scales_to_blocked_grouped(const uint8_t* s, int64_t rows, int64_t cols,
+                                       const int32_t* group_end_offsets, int32_t num_groups,
+                                       int32_t group_axis, uint8_t* out,
+                                       int64_t* out_group_starts, hipStream_t stream) {
+  if (num_groups < 1 || num_groups > MX_MAX_GROUPS || (group_axis != 0 && group_axis != 1))
+    return MX_ERR_GROUPS;
+  if (rows < 0 || cols < 0 || rows + 128 * (int64_t)num_groups >= INT_MAX ||
+      cols + 4 * (int64_t)num_groups >= INT_MAX)
+    return MX_ERR_SHAPE;
+  const int64_t bytes = mx_blocked_grouped_bytes(rows, cols, num_groups, group_axis);
+  if (group_end_offsets == nullptr || (out == nullptr && bytes > 0) ||
+      (s == nullptr && rows * cols > 0))
+    return MX_ERR_NULL;
+  if (out != nullptr && !aligned(out, 16))
+    return MX_ERR_ALIGN;
+  if (out_group_starts != nullptr && !aligned(out_group_starts, 8))
+    return MX_ERR_ALIGN;
+  if (!aligned(group_end_offsets, 4))
+    return MX_ERR_ALIGN;
+  return from_hip(mx::launch_blocked_grouped(s, rows, cols, group_end_offsets, num_groups,
+                                             group_axis, out, bytes, out_group_starts, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,23 @@
+// Internal launchers behind the C ABI (arguments already validated).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mx {
+
+// Cast kernel: rows x cols bf16; q0/s0 (dim0) and/or q1/s1 (dim1) non-null.
+// rows_per_seg splits the rows into segments whose dim1 outputs are stored
+// one after another (3D expert weights); pass rows for a plain 2D cast.
+hipError_t launch_cast_any(const uint16_t* x, int64_t rows, int64_t cols, int64_t rows_per_seg,
+                           uint8_t* q0, uint8_t* s0, uint8_t* q1, uint8_t* s1,
+                           hipStream_t stream);
+int64_t cast_grid_blocks(int64_t rows, int64_t cols);
+
+hipError_t launch_blocked_batched(const uint8_t* s, int64_t batch, int64_t rows, int64_t cols,
+                                  uint8_t* out, hipStream_t stream);
+hipError_t launch_blocked_grouped(const uint8_t* s, int64_t rows, int64_t cols, const int32_t* ends,
+                                  int32_t groups, int32_t axis, uint8_t* out, int64_t out_bytes,
+                                  int64_t* out_starts, hipStream_t stream);
+
+}  // namespace mx

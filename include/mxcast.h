@@ -1,0 +1,170 @@
+/*
+ * mxcast.h -- C ABI of libmxcast: bf16 -> MXFP8 casts and the 128x4 blocked
+ * e8m0 scale layout on AMD Instinct MI355X (gfx950).
+ *
+ * The method (pytorch/ao pull-request pages):
+ *  - "triton kernel to cast to mx across dim0 and dim1", Summary: cast a bf16
+ *    matrix to MX along dim0 and dim1 in 32-element blocks, writing the
+ *    row-major and the col-major results and both scale sets from a single
+ *    read of the input.
+ *  - "[mxfp8 moe training] add compile support": e8m0 scales rearranged into
+ *    the blocked layout per group along M (error trace: (16640, 160) scales,
+ *    int32 [G] and int64 [G+1] offsets), per group along K and per expert of
+ *    3D weights (Perf analysis, item 2); output rows bounded by rows +
+ *    num_groups * 128 so that no offset is read on the host (change list);
+ *    3D expert weights cast along dim1 through a 2D reshape (item 4).
+ *  - "[mxfp8 moe training] parallelize along col blocks in scale blocked
+ *    format kernel for groups along K", Changes: the blocked layout is built
+ *    at a granularity of 128x4 scales.
+ *
+ * MX rule (the pages do not spell it out; this is the reading implemented):
+ *   amax  = max |x| over a block of 32 (NaN > +Inf > finite);
+ *   e     = floor(log2(amax)) - 8, clamped to [-127, 127]; amax = 0 gives
+ *           e = -127; the scale byte is e + 127 (e8m0); a block holding a
+ *           NaN gets the e8m0 NaN byte 0xFF;
+ *   q     = x / 2^e rounded to nearest-even to e4m3fn, saturated to +-448
+ *           (so +-Inf -> +-448); in a NaN block every element is e4m3 NaN
+ *           with its own sign (0x7F / 0xFF).
+ *
+ * Blocked layout of a (rows, cols) scale matrix: rows padded to a multiple
+ * of 128, cols to a multiple of 4, padding bytes 0.  512-byte tiles of
+ * 128 rows x 4 cols, ordered by row block, then column block; inside a tile,
+ * scale (r, c) sits at byte (r % 32) * 16 + (r % 128 / 32) * 4 + c % 4.
+ *
+ * Conventions for every call below:
+ *  - All array arguments are DEVICE pointers, contiguous, row-major.
+ *  - The caller owns every buffer and the stream.  The library allocates
+ *    nothing, keeps no state, never synchronises and never reads device
+ *    memory from the host; all work is enqueued on `stream` (0 = the null
+ *    stream) and runs asynchronously.
+ *  - Arguments are validated on the host before any HIP call; a rejected
+ *    call enqueues nothing.  A launch failure reported by the HIP runtime
+ *    returns MX_ERR_HIP.
+ *  - Empty inputs (a zero extent) are valid and enqueue nothing; shapes are
+ *    checked first, so pointers may then be NULL.
+ */
+#ifndef MXCAST_H
+#define MXCAST_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#if defined(__GNUC__)
+#define MX_API __attribute__((visibility("default")))
+#else
+#define MX_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MX_OK = 0,
+    MX_ERR_NULL = 1,    /* a required pointer is NULL                          */
+    MX_ERR_SHAPE = 2,   /* a size is negative, not a multiple of 32 where one  */
+                        /* is required, or beyond the supported maximum        */
+    MX_ERR_GROUPS = 3,  /* num_groups outside [1, MX_MAX_GROUPS] or bad axis   */
+    MX_ERR_HIP = 4,     /* the HIP runtime rejected a launch                   */
+    MX_ERR_ALIGN = 5    /* a pointer lacks the alignment stated for it         */
+} mx_status;
+
+#define MX_BLOCK 32          /* elements per scale block                  */
+#define MX_MAX_GROUPS 1024   /* groups accepted by the grouped layout     */
+
+/* Static text for a status code. */
+MX_API const char* mx_status_string(mx_status status);
+
+/*
+ * bf16 -> MXFP8 along dim0 and dim1 from one read of the input.
+ *   x      bf16 (rows, cols) row-major; 16-byte aligned.
+ *   q_row  e4m3 (rows, cols): blocks of 32 along each row; 8-byte aligned.
+ *   s_row  e8m0 (rows, cols / 32).
+ *   q_col  e4m3 of the col-major cast: the (rows, cols) result in column-
+ *          major order, i.e. a row-major (cols, rows) array whose row c holds
+ *          column c of x cast in blocks of 32 consecutive rows; 16-byte
+ *          aligned.
+ *   s_col  e8m0 (cols, rows / 32).
+ * Either output pair may be NULL to skip that direction (both members of a
+ * pair NULL); both pairs NULL, a half-NULL pair or x NULL -> MX_ERR_NULL.
+ * rows and cols must be >= 0 and multiples of 32, else MX_ERR_SHAPE.
+ * Outputs must not overlap the input or each other.
+ */
+MX_API mx_status mx_cast_dim0_dim1(const void* x, int64_t rows, int64_t cols,
+                            uint8_t* q_row, uint8_t* s_row,
+                            uint8_t* q_col, uint8_t* s_col,
+                            hipStream_t stream);
+
+/*
+ * dim1 cast of 3D expert weights, expert by expert.
+ *   w  bf16 (experts, n, k) contiguous; 16-byte aligned.
+ *   q  e4m3 (experts, k, n): expert e's (n, k) matrix cast in blocks of 32
+ *      along n and stored col-major (row-major (k, n)); 16-byte aligned.
+ *   s  e8m0 (experts, k, n / 32).
+ * Because n is a multiple of 32, blocks never straddle experts and the
+ * values equal the 2D dim1 cast of the (experts * n, k) reshape.
+ * n or k not a multiple of 32, or a negative size -> MX_ERR_SHAPE.
+ */
+MX_API mx_status mx_cast_dim1_3d(const void* w, int64_t experts, int64_t n, int64_t k,
+                          uint8_t* q, uint8_t* s, hipStream_t stream);
+
+/* Bytes of the blocked form of `batch` (rows, cols) matrices:
+ * batch * ceil128(rows) * ceil4(cols); -1 on a negative argument. */
+MX_API int64_t mx_blocked_bytes(int64_t batch, int64_t rows, int64_t cols);
+
+/*
+ * Blocked layout of `batch` independent e8m0 (rows, cols) matrices.
+ *   s    u8 (batch, rows, cols).
+ *   out  mx_blocked_bytes(batch, rows, cols) bytes: matrix b's blocked form
+ *        at byte b * ceil128(rows) * ceil4(cols); every byte is written
+ *        (padding 0).
+ * batch = 1 is the plain 2D conversion; batch = experts converts the
+ * (experts, k, n / 32) scales of mx_cast_dim1_3d per expert.
+ */
+MX_API mx_status mx_scales_to_blocked(const uint8_t* s, int64_t batch, int64_t rows, int64_t cols,
+                               uint8_t* out, hipStream_t stream);
+
+/* Size in bytes of the grouped blocked output (host arithmetic only):
+ *   axis 0: (rows + 128 * num_groups) * ceil4(cols)
+ *   axis 1: ceil128(rows) * (ceil4(cols) + 4 * num_groups)
+ * -1 on a negative size, num_groups outside [1, MX_MAX_GROUPS] or a bad axis. */
+MX_API int64_t mx_blocked_grouped_bytes(int64_t rows, int64_t cols, int32_t num_groups,
+                                 int32_t group_axis);
+
+/*
+ * Grouped blocked layout with the group offsets kept on the device.
+ *   s                  u8 (rows, cols) scales.
+ *   group_end_offsets  DEVICE int32 [num_groups]: cumulative END offset of
+ *                      each group along the grouped axis, in rows of s
+ *                      (group_axis 0, "M groups") or in scale columns of s
+ *                      (group_axis 1, "K groups"); the last should equal the
+ *                      extent.  Empty groups are allowed.  The offsets are
+ *                      never read on the host; the kernel clamps each end to
+ *                      [previous end, extent] and ignores anything past the
+ *                      last end, so malformed offsets stay memory-safe.
+ *   out                mx_blocked_grouped_bytes(...) bytes, every byte
+ *                      written.  axis 0: group g padded to a multiple of 128
+ *                      rows, starting at output row start[g] (byte
+ *                      start[g] * ceil4(cols)); the whole buffer reads as one
+ *                      blocked matrix of rows + 128 * G rows.  axis 1: group
+ *                      g padded to a multiple of 4 columns and laid out as
+ *                      its own blocked matrix of ceil128(rows) rows at byte
+ *                      ceil128(rows) * start[g].  Bytes past the last group
+ *                      are 0.
+ *   out_group_starts   DEVICE int64 [num_groups + 1] or NULL: start[g] in
+ *                      output rows (axis 0) or output columns (axis 1);
+ *                      start[num_groups] is the padded total.
+ * rows, cols >= 0 (rows + 128 * G and cols + 4 * G below 2^31), group_axis
+ * 0 or 1, 1 <= num_groups <= MX_MAX_GROUPS; s, out and group_end_offsets
+ * non-NULL (s may be NULL only when rows * cols == 0).
+ */
+MX_API mx_status mx_scales_to_blocked_grouped(const uint8_t* s, int64_t rows, int64_t cols,
+                                       const int32_t* group_end_offsets, int32_t num_groups,
+                                       int32_t group_axis, uint8_t* out,
+                                       int64_t* out_group_starts, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXCAST_H */

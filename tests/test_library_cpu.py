@@ -1,0 +1,121 @@
+"""The C-ABI library on a machine without a GPU: it loads, exports every
+symbol the header declares, and rejects bad arguments on the host before any
+HIP call (no call here reaches a launch)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxcast.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_GROUPS, ERR_HIP, ERR_ALIGN = range(6)
+P = ctypes.c_void_p(0x10000)       # well aligned, never dereferenced
+P_ODD = ctypes.c_void_p(0x10001)   # misaligned
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import fp8_precision_quantization_amd as mx
+    from fp8_precision_quantization_amd import build
+    if not os.path.exists(mx.LIB_PATH):
+        build.build()
+    return mx.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"MX_API\s+[\w\s\*]+?\b(mx_\w+)\s*\(", text)
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == {"mx_status_string", "mx_cast_dim0_dim1", "mx_cast_dim1_3d",
+                          "mx_blocked_bytes", "mx_scales_to_blocked",
+                          "mx_blocked_grouped_bytes", "mx_scales_to_blocked_grouped"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for s in range(6):
+        assert lib.mx_status_string(s)
+    assert b"unknown" in lib.mx_status_string(99)
+
+
+def test_cast_dim0_dim1_validation(lib):
+    f = lib.mx_cast_dim0_dim1
+    assert f(None, 32, 32, P, P, P, P, None) == ERR_NULL
+    assert f(P, 32, 32, None, None, None, None, None) == ERR_NULL      # no output pair
+    assert f(None, 33, 32, P, P, P, P, None) == ERR_SHAPE              # shape first
+    assert f(P, 32, 32, P, None, None, None, None) == ERR_NULL         # half pair
+    assert f(P, 32, 32, None, None, None, P, None) == ERR_NULL
+    for r, c in [(33, 32), (32, 48), (-32, 32), (32, -32), (1 << 41, 32)]:
+        assert f(P, r, c, P, P, P, P, None) == ERR_SHAPE, (r, c)
+    assert f(P_ODD, 32, 32, P, P, P, P, None) == ERR_ALIGN
+    assert f(P, 32, 32, P, P, ctypes.c_void_p(0x10008), P, None) == ERR_ALIGN
+    assert f(P, 32, 32, ctypes.c_void_p(0x10004), P, None, None, None) == ERR_ALIGN
+    # empty extents are accepted and enqueue nothing
+    assert f(P, 0, 64, P, P, P, P, None) == OK
+    assert f(P, 64, 0, P, P, P, P, None) == OK
+    assert f(None, 0, 0, None, None, None, None, None) == OK
+
+
+def test_cast_dim1_3d_validation(lib):
+    f = lib.mx_cast_dim1_3d
+    assert f(None, 2, 32, 32, P, P, None) == ERR_NULL
+    assert f(P, 2, 32, 32, None, P, None) == ERR_NULL
+    assert f(P, 2, 48, 32, P, P, None) == ERR_SHAPE
+    assert f(P, 2, 32, 40, P, P, None) == ERR_SHAPE
+    assert f(P, -1, 32, 32, P, P, None) == ERR_SHAPE
+    assert f(P_ODD, 2, 32, 32, P, P, None) == ERR_ALIGN
+    assert f(P, 0, 32, 32, P, P, None) == OK
+    assert f(None, 0, 32, 32, None, None, None) == OK
+
+
+def test_blocked_sizes_match_oracle(lib, oracle_mod):
+    for b, r, c in [(1, 1, 1), (1, 130, 7), (3, 256, 8), (16, 5120, 256), (2, 0, 5)]:
+        assert lib.mx_blocked_bytes(b, r, c) == b * oracle_mod.blocked_size(r, c)
+    assert lib.mx_blocked_bytes(-1, 4, 4) == -1
+    for r, c, g, a in [(16640, 160, 4, 0), (5120, 512, 4, 1), (100, 5, 2, 1), (0, 0, 1, 0),
+                       (7, 9, 1024, 0), (7, 9, 1024, 1)]:
+        assert lib.mx_blocked_grouped_bytes(r, c, g, a) == oracle_mod.blocked_grouped_size(r, c, g, a)
+    assert lib.mx_blocked_grouped_bytes(10, 10, 0, 0) == -1
+    assert lib.mx_blocked_grouped_bytes(10, 10, 1025, 0) == -1
+    assert lib.mx_blocked_grouped_bytes(10, 10, 1, 2) == -1
+    assert lib.mx_blocked_grouped_bytes(-1, 10, 1, 0) == -1
+
+
+def test_scales_to_blocked_validation(lib):
+    f = lib.mx_scales_to_blocked
+    assert f(P, -1, 4, 4, P, None) == ERR_SHAPE
+    assert f(P, 1, 4, 4, None, None) == ERR_NULL
+    assert f(None, 1, 4, 4, P, None) == ERR_NULL
+    assert f(P, 1, 4, 4, P_ODD, None) == ERR_ALIGN
+    assert f(P, 0, 4, 4, P, None) == OK
+
+
+def test_scales_to_blocked_grouped_validation(lib):
+    f = lib.mx_scales_to_blocked_grouped
+    assert f(P, 64, 8, P, 0, 0, P, P, None) == ERR_GROUPS
+    assert f(P, 64, 8, P, 1025, 0, P, P, None) == ERR_GROUPS
+    assert f(P, 64, 8, P, 1, 2, P, P, None) == ERR_GROUPS
+    assert f(P, -1, 8, P, 1, 0, P, P, None) == ERR_SHAPE
+    assert f(P, (1 << 31) - 100, 8, P, 1, 0, P, P, None) == ERR_SHAPE
+    assert f(P, 64, 8, None, 1, 0, P, P, None) == ERR_NULL
+    assert f(P, 64, 8, P, 1, 0, None, P, None) == ERR_NULL
+    assert f(None, 64, 8, P, 1, 0, P, P, None) == ERR_NULL
+    assert f(P, 64, 8, P, 1, 0, P_ODD, P, None) == ERR_ALIGN
+    assert f(P, 64, 8, P, 1, 0, P, ctypes.c_void_p(0x10004), None) == ERR_ALIGN
+    assert f(P, 64, 8, P_ODD, 1, 0, P, P, None) == ERR_ALIGN
+
+
+def test_python_binding_requires_gpu_tensors():
+    import torch
+    import fp8_precision_quantization_amd as mx
+    with pytest.raises(ValueError):
+        mx.mx_cast_dim0_dim1(torch.zeros((32, 32), dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        mx.mx_scales_to_blocked(torch.zeros((4, 4), dtype=torch.uint8))
