@@ -1,0 +1,314 @@
+"""Benchmark of the MXFP8 hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one pass of the hot path over one batch of synthetic input held
+in HBM.  The default workload is the headline one: the bf16 -> MXFP8 dim0 +
+dim1 cast of a 16384 x 16384 matrix with heavy-tailed rows, followed by the
+128x4 blocked layout of both scale sets.  Other workloads (for profiling):
+  moe16640   cast of (16640, 5120) activations + M-grouped layout of the row
+             scales (4 groups along M, offsets on the device);
+  kgroups    K-grouped layouts of (5120, 512), (8192, 4096), (2048, 4096)
+             scale tensors (4 groups along K);
+  experts16  dim1 cast of (16, 8192, 5120) expert weights + per-expert
+             blocked layout of their scales;
+  copy       a plain device-to-device copy of 1 GiB (counter calibration).
+
+Prints exactly one JSON line on stdout; progress goes to stderr.  The
+`roofline` object is for the dominant kernel (the cast): algorithmic bytes per
+launch divided by its average duration from HIP events recorded on the stream
+it runs on.  `cpu_baseline` times the CPU oracle on a bounded slice of the
+same input (rank 0, one GPU) and checks that slice against the GPU output.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import fp8_precision_quantization_amd as mx  # noqa: E402
+from fp8_precision_quantization_amd import workloads  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "achieved HBM GB/s (% of MI355X peak) for bf16→MXFP8 dim0+dim1 cast"
+CAST_SOURCES = ["fp8_precision_quantization_amd/csrc/mx_cast.hip",
+                "fp8_precision_quantization_amd/csrc/mx_device.h"]
+COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "cast_square16384_counters.md")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def pad(v, m):
+    return -(-v // m) * m
+
+
+def to_dev_bf16(bits, dev):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def cast_bytes(rows, cols):
+    """Algorithmic bytes of the dim0+dim1 cast: read 2 B, write 1 + 1 B per
+    element, plus one e8m0 byte per 32 elements in each direction."""
+    return rows * cols * 2 + 2 * rows * cols + 2 * (rows * cols // 32)
+
+
+def blocked_bytes(rows, cols, batch=1):
+    return batch * (rows * cols + pad(rows, 128) * pad(cols, 4))
+
+
+def sources_digest():
+    h = hashlib.sha256()
+    for p in CAST_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic():
+    """HBM bytes per cast launch from the committed counter summary, or None
+    when it is missing or was taken on different kernel sources."""
+    try:
+        text = open(COUNTER_SUMMARY).read()
+    except OSError:
+        return None
+    m_sha = re.search(r"kernel_sources_sha256:\s*([0-9a-f]+)", text)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.]+)", text)
+    if not m_sha or not m_b or m_sha.group(1) != sources_digest():
+        return None
+    return float(m_b.group(1))
+
+
+class Timer:
+    """HIP events bracketing one kernel on torch's current stream (the stream
+    the library launches on)."""
+
+    def __init__(self):
+        self.pairs = []
+
+    def __enter__(self):
+        self.a = torch.cuda.Event(enable_timing=True)
+        self.b = torch.cuda.Event(enable_timing=True)
+        self.a.record()
+        return self
+
+    def __exit__(self, *exc):
+        self.b.record()
+        self.pairs.append((self.a, self.b))
+
+    def mean_ms(self):
+        return sum(a.elapsed_time(b) for a, b in self.pairs) / len(self.pairs)
+
+
+# --------------------------------------------------------------------------
+# workloads
+# --------------------------------------------------------------------------
+def setup_square(dev, n=16384):
+    log("generating %dx%d heavy-tailed bf16 input" % (n, n))
+    bits = workloads.heavy_tailed_rows(n, n, seed=2)
+    x = to_dev_bf16(bits, dev)
+    q0 = torch.empty((n, n), dtype=torch.uint8, device=dev)
+    s0 = torch.empty((n, n // 32), dtype=torch.uint8, device=dev)
+    q1 = torch.empty((n, n), dtype=torch.uint8, device=dev)
+    s1 = torch.empty((n, n // 32), dtype=torch.uint8, device=dev)
+    b0 = torch.empty((pad(n, 128), pad(n // 32, 4)), dtype=torch.uint8, device=dev)
+    b1 = torch.empty_like(b0)
+    timer = Timer()
+
+    def step():
+        with timer:
+            mx.mx_cast_dim0_dim1(x, out=(q0, s0, q1, s1), raw=True)
+        mx.mx_scales_to_blocked(s0, out=b0, raw=True)
+        mx.mx_scales_to_blocked(s1, out=b1, raw=True)
+
+    step_bytes = cast_bytes(n, n) + 2 * blocked_bytes(n, n // 32)
+
+    def cpu_baseline():
+        import oracle
+        rows = 4096
+        sample = np.ascontiguousarray(bits[:rows])
+        t0 = time.perf_counter()
+        r_q0, r_s0 = oracle.cast_dim0(sample)
+        r_q1, r_s1 = oracle.cast_dim1(sample)
+        oracle.to_blocked(r_s0)
+        oracle.to_blocked(r_s1)
+        dt = time.perf_counter() - t0
+        nbytes = cast_bytes(rows, n) + blocked_bytes(rows, n // 32) + blocked_bytes(n, rows // 32)
+        ok = (np.array_equal(q0[:rows].cpu().numpy(), r_q0)
+              and np.array_equal(s0[:rows].cpu().numpy(), r_s0)
+              and np.array_equal(q1[:, :rows].cpu().numpy(), r_q1)
+              and np.array_equal(s1[:, :rows // 32].cpu().numpy(), r_s1))
+        return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
+                "kind": "oracle",
+                "sample": "rows 0..%d of the %dx%d input (dim0+dim1 cast + blocked layout of "
+                          "both scale sets), %.1f s wall" % (rows, n, n, dt),
+                "matches_gpu": bool(ok)}
+
+    config = {"workload": "mx_cast_dim0_dim1 %dx%d bf16 (heavy-tailed rows) + blocked "
+                          "layout of both scale sets" % (n, n),
+              "rows": n, "cols": n, "block": 32, "elem": "e4m3", "scale": "e8m0"}
+    return step, step_bytes, timer, cast_bytes(n, n), "cast dim0+dim1", cpu_baseline, config
+
+
+def setup_moe(dev):
+    bits, ends = workloads.moe_activations()
+    rows, cols = bits.shape
+    x = to_dev_bf16(bits, dev)
+    offs = torch.from_numpy(ends).to(dev)
+    q0 = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+    s0 = torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev)
+    q1 = torch.empty((cols, rows), dtype=torch.uint8, device=dev)
+    s1 = torch.empty((cols, rows // 32), dtype=torch.uint8, device=dev)
+    g = len(ends)
+    out = torch.empty((rows + 128 * g, pad(cols // 32, 4)), dtype=torch.uint8, device=dev)
+    starts = torch.empty(g + 1, dtype=torch.int64, device=dev)
+    timer = Timer()
+
+    def step():
+        with timer:
+            mx.mx_cast_dim0_dim1(x, out=(q0, s0, q1, s1), raw=True)
+        mx.mx_scales_to_blocked_grouped(s0, offs, 0, out=out, out_group_starts=starts, raw=True)
+
+    nb = cast_bytes(rows, cols) + rows * (cols // 32) + out.numel()
+    config = {"workload": "mx_cast_dim0_dim1 %dx%d bf16 + M-grouped blocked layout (%d groups)"
+                          % (rows, cols, g), "rows": rows, "cols": cols, "groups": g}
+    return step, nb, timer, cast_bytes(rows, cols), "cast dim0+dim1", None, config
+
+
+def setup_kgroups(dev):
+    items = []
+    for shape in workloads.K_GROUP_SHAPES:
+        s, ends = workloads.k_group_scales(shape)
+        r, c = shape
+        g = len(ends)
+        items.append((torch.from_numpy(s).to(dev), torch.from_numpy(ends).to(dev),
+                      torch.empty((pad(r, 128), pad(c, 4) + 4 * g), dtype=torch.uint8, device=dev),
+                      torch.empty(g + 1, dtype=torch.int64, device=dev)))
+    timer = Timer()
+
+    def step():
+        for i, (s, offs, out, starts) in enumerate(items):
+            if i == 1:
+                with timer:
+                    mx.mx_scales_to_blocked_grouped(s, offs, 1, out=out, out_group_starts=starts,
+                                                    raw=True)
+            else:
+                mx.mx_scales_to_blocked_grouped(s, offs, 1, out=out, out_group_starts=starts, raw=True)
+
+    nb = sum(s.numel() + out.numel() for s, _, out, _ in items)
+    big = items[1][0].numel() + items[1][2].numel()
+    config = {"workload": "K-grouped blocked layout of e8m0 scales %s, 4 groups each"
+                          % (list(workloads.K_GROUP_SHAPES),)}
+    return step, nb, timer, big, "K-grouped layout (8192, 4096)", None, config
+
+
+def setup_experts(dev, experts=16, n=8192, k=5120):
+    log("generating (%d, %d, %d) expert weights" % (experts, n, k))
+    w = torch.empty((experts, n, k), dtype=torch.bfloat16, device=dev)
+    for e in range(experts):
+        w[e] = to_dev_bf16(workloads.expert_weight(e, n, k), dev)
+    q = torch.empty((experts, k, n), dtype=torch.uint8, device=dev)
+    s = torch.empty((experts, k, n // 32), dtype=torch.uint8, device=dev)
+    out = torch.empty((experts, pad(k, 128), pad(n // 32, 4)), dtype=torch.uint8, device=dev)
+    timer = Timer()
+
+    def step():
+        with timer:
+            mx.mx_cast_dim1_3d(w, out=(q, s), raw=True)
+        mx.mx_scales_to_blocked(s, out=out, raw=True)
+
+    cb = experts * n * k * 3 + experts * n * k // 32
+    nb = cb + blocked_bytes(k, n // 32, experts)
+    config = {"workload": "mx_cast_dim1_3d (%d, %d, %d) bf16 + per-expert blocked layout"
+                          % (experts, n, k), "experts": experts, "n": n, "k": k}
+    return step, nb, timer, cb, "cast dim1 3D", None, config
+
+
+def setup_copy(dev, nbytes=1 << 30):
+    a = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    b = torch.empty_like(a)
+    timer = Timer()
+
+    def step():
+        with timer:
+            b.copy_(a)
+
+    config = {"workload": "device copy of %d bytes (counter calibration)" % nbytes}
+    return step, 2 * nbytes, timer, 2 * nbytes, "copy", None, config
+
+
+WORKLOADS = {"square16384": setup_square, "moe16640": setup_moe, "kgroups": setup_kgroups,
+             "experts16": setup_experts, "copy": setup_copy}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="square16384", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the cast and layout kernels run on one GPU's "
+              "share and no multi-GPU path is built; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    mx.lib()
+
+    step, step_bytes, timer, kern_bytes, kern_name, cpu_fn, config = WORKLOADS[args.workload](dev)
+    torch.cuda.synchronize(dev)
+    log("warmup %d steps" % args.warmup)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    timer.pairs.clear()
+
+    log("timing %d steps" % args.steps)
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize(dev)
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    kern_ms = timer.mean_ms()
+    achieved = kern_bytes / (kern_ms * 1e-3) / 1e9
+    log("step %.2f us, %s %.2f us = %.1f GB/s" % (ms_per_step * 1e3, kern_name, kern_ms * 1e3,
+                                                  achieved))
+
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": counter_traffic() if args.workload == "square16384" else None,
+                "kernel": kern_name, "kernel_us": round(kern_ms * 1e3, 2),
+                "algorithmic_bytes": kern_bytes}
+
+    cpu = None
+    if cpu_fn is not None and not args.no_cpu_baseline:
+        log("timing the CPU oracle on a slice")
+        cpu = cpu_fn()
+
+    line = {"metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic", "config": config, "roofline": roofline, "cpu_baseline": cpu}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

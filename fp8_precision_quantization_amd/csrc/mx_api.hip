@@ -9,6 +9,9 @@
 namespace {
 
 constexpr int64_t kMaxExtent = (int64_t)1 << 40;  // per-dimension bound, keeps products in int64
+// The cast kernels address 32 rows of a row-major matrix from one scalar base
+// with 32-bit row offsets: 32 * cols * 2 bytes must stay below 2^31.
+constexpr int64_t kMaxCastCols = (int64_t)1 << 25;
 constexpr int64_t kMaxGridBlocks = INT_MAX;
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
@@ -35,7 +38,7 @@ const char* mx_status_string(mx_status status) {
 mx_status mx_cast_dim0_dim1(const void* x, int64_t rows, int64_t cols, uint8_t* q_row,
                             uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, hipStream_t stream) {
   if (rows < 0 || cols < 0 || rows % MX_BLOCK != 0 || cols % MX_BLOCK != 0 || rows > kMaxExtent ||
-      cols > kMaxExtent)
+      cols > kMaxCastCols)
     return MX_ERR_SHAPE;
   if (rows == 0 || cols == 0)
     return MX_OK;  // nothing to read or write; the pointers may be NULL
@@ -57,7 +60,7 @@ mx_status mx_cast_dim0_dim1(const void* x, int64_t rows, int64_t cols, uint8_t* 
 mx_status mx_cast_dim1_3d(const void* w, int64_t experts, int64_t n, int64_t k, uint8_t* q,
                           uint8_t* s, hipStream_t stream) {
   if (experts < 0 || n < 0 || k < 0 || n % MX_BLOCK != 0 || k % MX_BLOCK != 0 ||
-      experts > kMaxExtent || n > kMaxExtent || k > kMaxExtent ||
+      experts > kMaxExtent || n > kMaxExtent || k > kMaxCastCols ||
       (n > 0 && experts > kMaxExtent / n))
     return MX_ERR_SHAPE;
   if (experts == 0 || n == 0 || k == 0)

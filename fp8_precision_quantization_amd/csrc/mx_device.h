@@ -14,6 +14,8 @@ namespace mx {
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t kMagMask2 = 0x7FFF7FFFu;  // clears both sign bits
 constexpr uint32_t kInfBits = 0x7F80u;         // bf16 +Inf magnitude
@@ -22,6 +24,22 @@ __device__ __forceinline__ u16x2 as_u16x2(uint32_t v) { return __builtin_bit_cas
 __device__ __forceinline__ uint32_t as_u32(u16x2 v) { return __builtin_bit_cast(uint32_t, v); }
 __device__ __forceinline__ i16x2 as_i16x2(uint32_t v) { return __builtin_bit_cast(i16x2, v); }
 __device__ __forceinline__ uint32_t as_u32(i16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+
+// Raw buffer resource over [base, base + bytes) for buffer loads and stores
+// whose row offset sits in a scalar register (no per-lane address math).
+// The third descriptor word is the gfx950 raw-buffer format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// Global accesses of the streaming kernels.  They stay ordinary (cached)
+// accesses: non-temporal stores keep the L2 from merging the partial lines
+// that neighbouring lanes and waves write, which multiplies HBM writes.
+__device__ __forceinline__ uint2 load_stream(const uint2* p) { return *p; }
+__device__ __forceinline__ void store_stream(uint4* p, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  *reinterpret_cast<u32x4*>(p) = (u32x4){a, b, c, d};
+}
+__device__ __forceinline__ void store_stream(uint32_t* p, uint32_t v) { *p = v; }
 
 // Per-half unsigned max of two packed 16-bit pairs (v_pk_max_u16).
 __device__ __forceinline__ uint32_t max2(uint32_t a, uint32_t b) {

@@ -87,8 +87,8 @@ MX_API const char* mx_status_string(mx_status status);
  *   s_col  e8m0 (cols, rows / 32).
  * Either output pair may be NULL to skip that direction (both members of a
  * pair NULL); both pairs NULL, a half-NULL pair or x NULL -> MX_ERR_NULL.
- * rows and cols must be >= 0 and multiples of 32, else MX_ERR_SHAPE.
- * Outputs must not overlap the input or each other.
+ * rows and cols must be >= 0 and multiples of 32, cols <= 2^25, else
+ * MX_ERR_SHAPE.  Outputs must not overlap the input or each other.
  */
 MX_API mx_status mx_cast_dim0_dim1(const void* x, int64_t rows, int64_t cols,
                             uint8_t* q_row, uint8_t* s_row,
@@ -103,7 +103,7 @@ MX_API mx_status mx_cast_dim0_dim1(const void* x, int64_t rows, int64_t cols,
  *   s  e8m0 (experts, k, n / 32).
  * Because n is a multiple of 32, blocks never straddle experts and the
  * values equal the 2D dim1 cast of the (experts * n, k) reshape.
- * n or k not a multiple of 32, or a negative size -> MX_ERR_SHAPE.
+ * n or k not a multiple of 32, k > 2^25, or a negative size -> MX_ERR_SHAPE.
  */
 MX_API mx_status mx_cast_dim1_3d(const void* w, int64_t experts, int64_t n, int64_t k,
                           uint8_t* q, uint8_t* s, hipStream_t stream);

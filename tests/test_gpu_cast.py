@@ -42,7 +42,7 @@ def test_square_with_special_tiles(oracle_mod):
 
 
 SHAPES = [(32, 32), (32, 256), (64, 96), (96, 288), (128, 256), (160, 544), (256, 800),
-          (416, 1056), (1024, 32), (32, 2080)]
+          (416, 1056), (1024, 32), (32, 2080), (1568, 1056), (544, 3104), (2048, 64)]
 
 
 @pytest.mark.parametrize("shape", SHAPES)
@@ -140,7 +140,8 @@ def test_rejects_bad_shapes():
         assert e.value.status == 2
 
 
-@pytest.mark.parametrize("e,n,k", [(3, 64, 96), (2, 160, 288), (4, 256, 512), (1, 32, 32)])
+@pytest.mark.parametrize("e,n,k", [(3, 64, 96), (2, 160, 288), (4, 256, 512), (1, 32, 32),
+                                   (3, 544, 64), (2, 1024, 1056), (5, 96, 2080)])
 def test_dim1_3d(oracle_mod, e, n, k):
     dev = device()
     w = workloads.special_values_bf16((e * n, k), seed=e * 100 + n, p_special=0.001).reshape(e, n, k)

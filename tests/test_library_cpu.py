@@ -52,7 +52,7 @@ def test_cast_dim0_dim1_validation(lib):
     assert f(None, 33, 32, P, P, P, P, None) == ERR_SHAPE              # shape first
     assert f(P, 32, 32, P, None, None, None, None) == ERR_NULL         # half pair
     assert f(P, 32, 32, None, None, None, P, None) == ERR_NULL
-    for r, c in [(33, 32), (32, 48), (-32, 32), (32, -32), (1 << 41, 32)]:
+    for r, c in [(33, 32), (32, 48), (-32, 32), (32, -32), (1 << 41, 32), (32, (1 << 25) + 32)]:
         assert f(P, r, c, P, P, P, P, None) == ERR_SHAPE, (r, c)
     assert f(P_ODD, 32, 32, P, P, P, P, None) == ERR_ALIGN
     assert f(P, 32, 32, P, P, ctypes.c_void_p(0x10008), P, None) == ERR_ALIGN
