@@ -1,0 +1,106 @@
+"""GPU parity at the full sizes of the five workloads, in the launch
+configuration the benchmark times, against the CPU oracle on the same seeded
+inputs (bytes, tolerance 0).
+
+  1. 1024 x 1024 N(0,1) with zero / denormal / outlier tiles  (test_gpu_cast)
+  2. 16384 x 16384 heavy-tailed rows: dim0+dim1 cast + blocked scales, in full
+  3. 16640 x 5120 MoE activations: cast + M-grouped scales (4 groups), in full
+  4. K-grouped scale layouts of (5120, 512), (8192, 4096), (2048, 4096), in full
+  5. (16, 8192, 5120) expert weights: dim1 3D cast + per-expert blocked scales,
+     all experts on the GPU, three of them compared in full
+"""
+import numpy as np
+import pytest
+import torch
+
+import fp8_precision_quantization_amd as mx
+from fp8_precision_quantization_amd import workloads
+from tests.gpu_util import assert_bytes_equal, device, host, to_dev_bf16, to_dev_u8
+
+pytestmark = pytest.mark.gpu
+
+
+def _pad(v, m):
+    return -(-v // m) * m
+
+
+def test_square_16384_heavy_tailed(oracle_mod):
+    dev = device()
+    bits = workloads.heavy_tailed_rows(16384, 16384, seed=2)
+    x = to_dev_bf16(bits, dev)
+    q0, s0, q1, s1 = mx.mx_cast_dim0_dim1(x, raw=True)
+    b0 = mx.mx_scales_to_blocked(s0, raw=True)
+    b1 = mx.mx_scales_to_blocked(s1, raw=True)
+    torch.cuda.synchronize(dev)
+    del x
+    r_q0, r_s0 = oracle_mod.cast_dim0(bits)
+    assert_bytes_equal(host(s0), r_s0, "16384^2 s_row")
+    assert_bytes_equal(host(q0), r_q0, "16384^2 q_row")
+    assert_bytes_equal(host(b0).reshape(-1), oracle_mod.to_blocked(r_s0), "16384^2 blocked s_row")
+    del r_q0, q0
+    r_q1, r_s1 = oracle_mod.cast_dim1(bits)
+    assert_bytes_equal(host(s1), r_s1, "16384^2 s_col")
+    assert_bytes_equal(host(q1), r_q1, "16384^2 q_col")
+    assert_bytes_equal(host(b1).reshape(-1), oracle_mod.to_blocked(r_s1), "16384^2 blocked s_col")
+    # heavy-tailed rows spread the row scales over ~two dozen binades; column
+    # blocks take the max over 32 rows and so sit in fewer, higher ones
+    assert len(np.unique(r_s0)) >= 20 and len(np.unique(r_s1)) >= 10
+
+
+def test_moe_activations_m_groups(oracle_mod):
+    dev = device()
+    bits, ends = workloads.moe_activations()
+    rows, cols = bits.shape
+    assert (rows, cols) == (16640, 5120) and ends[-1] == rows and np.all(np.diff(ends) > 0)
+    x = to_dev_bf16(bits, dev)
+    q0, s0, q1, s1 = mx.mx_cast_dim0_dim1(x, raw=True)
+    offs = torch.from_numpy(ends).to(dev)
+    grouped, starts = mx.mx_scales_to_blocked_grouped(s0, offs, 0, raw=True)
+    torch.cuda.synchronize(dev)
+    assert tuple(s0.shape) == (16640, 160)
+    assert tuple(grouped.shape) == (16640 + 4 * 128, 160)
+    r_q0, r_s0 = oracle_mod.cast_dim0(bits)
+    r_q1, r_s1 = oracle_mod.cast_dim1(bits)
+    assert_bytes_equal(host(q0), r_q0, "moe q_row")
+    assert_bytes_equal(host(s0), r_s0, "moe s_row")
+    assert_bytes_equal(host(q1), r_q1, "moe q_col")
+    assert_bytes_equal(host(s1), r_s1, "moe s_col")
+    r_g, r_starts = oracle_mod.to_blocked_grouped(r_s0, ends, 0)
+    assert_bytes_equal(host(grouped).reshape(-1), r_g, "moe M-grouped")
+    assert_bytes_equal(host(starts), r_starts, "moe starts")
+
+
+@pytest.mark.parametrize("shape", workloads.K_GROUP_SHAPES)
+def test_k_groups(oracle_mod, shape):
+    dev = device()
+    s, ends = workloads.k_group_scales(shape)
+    assert s.min() >= 100 and s.max() <= 140 and np.all(ends % 4 == 0)
+    out, starts = mx.mx_scales_to_blocked_grouped(to_dev_u8(s, dev), torch.from_numpy(ends).to(dev), 1,
+                                                  raw=True)
+    torch.cuda.synchronize(dev)
+    r_out, r_starts = oracle_mod.to_blocked_grouped(s, ends, 1)
+    assert_bytes_equal(host(out).reshape(-1), r_out, "K-grouped %s" % (shape,))
+    assert_bytes_equal(host(starts), r_starts, "K starts %s" % (shape,))
+
+
+def test_expert_weights_dim1_3d(oracle_mod):
+    dev = device()
+    e, n, k = 16, 8192, 5120
+    checked = {0: None, 7: None, 15: None}
+    w = torch.empty((e, n, k), dtype=torch.bfloat16, device=dev)
+    for i in range(e):
+        bits = workloads.expert_weight(i, n, k)
+        w[i] = to_dev_bf16(bits, dev)
+        if i in checked:
+            checked[i] = bits
+    q, s = mx.mx_cast_dim1_3d(w, raw=True)
+    blk = mx.mx_scales_to_blocked(s, raw=True)
+    torch.cuda.synchronize(dev)
+    del w
+    assert tuple(q.shape) == (e, k, n) and tuple(s.shape) == (e, k, n // 32)
+    assert tuple(blk.shape) == (e, _pad(k, 128), _pad(n // 32, 4))
+    for i, bits in checked.items():
+        r_q, r_s = oracle_mod.cast_dim1(bits)
+        assert_bytes_equal(host(q[i]), r_q, "expert %d q" % i)
+        assert_bytes_equal(host(s[i]), r_s, "expert %d s" % i)
+        assert_bytes_equal(host(blk[i]).reshape(-1), oracle_mod.to_blocked(r_s), "expert %d blocked" % i)
