@@ -5,129 +5,192 @@
 //
 // Work decomposition (gfx950, wave64):
 //   workgroup = 4 waves stacked along rows = a 128-row x 256-column tile;
-//   wave      = 32 rows x 256 columns: exactly one dim1 block height;
-//   lane      = 32 rows x 4 columns, loaded as 32 x 8-byte row segments.
-// Each row segment of a wave is 512 contiguous bytes, so every load is fully
-// coalesced.  A dim0 block (32 columns of one row) spans eight lanes and is
-// reduced with three DPP moves; a dim1 block (32 rows of one column) lives in
-// one lane, so its amax is a tree of packed 16-bit maxes.
+//   wave      = 32 rows x 256 columns, one dim1 block height: lanes 0-31 hold
+//               rows 0-15 and lanes 32-63 rows 16-31 of the same columns;
+//   lane      = 16 rows x 8 columns, loaded as 16 x 16-byte row segments.
+// Each load instruction of a wave reads two 512-byte row segments.  A dim0
+// block (32 columns of one row) spans a quad of lanes and is reduced with two
+// DPP moves; a dim1 block (32 rows of one column) is split between lanes l and
+// l + 32: an in-lane tree of packed 16-bit maxes, then one permlane32 swap.
+// The magnitudes are formed once and feed both reductions.
 //
 // Stores are shaped for the memory system rather than for the lanes that
 // produce them.  dim0 codes leave each wave as 256-byte row segments.  The
-// dim1 codes of a column (32 bytes per wave) are staged in LDS, and once the
+// dim1 codes of a column (16 bytes per lane) are staged in LDS, and once the
 // four waves are done the workgroup writes each column's 128 rows as one full
 // 128-byte line, eight lanes x 16 bytes per line; dim1 scale bytes are staged
 // the same way and leave as one 4-byte run per column.  Workgroups are
 // numbered so that the 32 tiles of one column range that share the lines of
 // the dim1 scale matrix run back to back on the same XCD (workgroups are
 // dispatched round-robin over the 8 XCDs), where that XCD's L2 merges them.
+#include <type_traits>
+
 #include "mx_device.h"
 #include "mxcast.h"
 #include "mx_launch.h"
 
 namespace mx {
 
+constexpr int kLaneRows = 16;
 constexpr int kWaveRows = 32;
 constexpr int kWaves = 4;
 constexpr int kTileRows = kWaves * kWaveRows;   // 128
-constexpr int kLaneCols = 4;
-constexpr int kTileCols = 64 * kLaneCols;       // 256
+constexpr int kLaneCols = 8;
+constexpr int kTileCols = 32 * kLaneCols;       // 256
 constexpr int kXcds = 8;
 constexpr int kRowGroup = 32;                   // row tiles sharing one dim1 scale line
+constexpr int kWalk = 8;                        // tiles per workgroup along the columns
 constexpr int kSlots = kTileRows / 16;          // 16-byte slots per staged column (8)
 
-__device__ __forceinline__ uint32_t half_of(const uint2& v, int k) { return k == 0 ? v.x : v.y; }
-
-// Column maxima of the tile's magnitudes for columns (2k, 2k+1), k = 0, 1,
-// by a balanced tree of independent maxes.
-__device__ __forceinline__ void column_max(const uint2 (&d)[kWaveRows], uint32_t (&cm)[2]) {
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    uint32_t t[kWaveRows / 2];
-#pragma unroll
-    for (int i = 0; i < kWaveRows / 2; ++i)
-      t[i] = max2(mag2(half_of(d[2 * i], k)), mag2(half_of(d[2 * i + 1], k)));
-#pragma unroll
-    for (int w = kWaveRows / 4; w >= 1; w >>= 1)
-#pragma unroll
-      for (int i = 0; i < w; ++i)
-        t[i] = max2(t[i], t[i + w]);
-    cm[k] = t[0];
-  }
+__device__ __forceinline__ uint32_t word(const uint4& v, int k) {
+  return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
 }
 
 // LDS slot of 16 dim1 codes: column col (0..255), rows 16 * slot .. +15 of
 // the tile.  The slot index is XOR-swizzled with bits of the column so that
 // the eight lanes of a 128-byte LDS access hit eight different bank groups
-// both when the producing lanes (consecutive columns) write and when the
-// storing lanes (one column, eight slots) read.
-__device__ __forceinline__ int q1_slot(int col, int slot) { return col * kSlots + (slot ^ ((col >> 2) & 7)); }
+// both when the producing lanes (columns 8 apart) write and when the storing
+// lanes (one column, eight slots) read.
+__device__ __forceinline__ int q1_slot(int col, int slot) { return col * kSlots + (slot ^ ((col >> 3) & 7)); }
 
-// dim0 of a wave's 32 rows: per row pair, the block amax over 8 lanes, then 4
-// codes per lane (one 256-byte row segment per wave) and one scale byte per
-// 8 lanes.
+// Finite-path parameters of two blocks at once: m holds two 15-bit amax
+// patterns [a, b].  For each: byte = max(E - 8, 0) (E = exponent field), the
+// clamp limit ((byte + 8) << 7) | 0x60 = bf16 pattern of 448 * 2^e, and the
+// convert's scale operand.  The convert reads only the exponent field of
+// that operand, so the limit shifted into place minus 8 << 23 is the scale.
+struct PairParams {
+  uint32_t t2_a, t2n_a, t2_b, t2n_b;
+  float scale_a, scale_b;
+};
+__device__ __forceinline__ PairParams pair_params(uint32_t m) {
+  PairParams p;
+  const uint32_t t = max2(m & 0x7F807F80u, 0x04000400u) | 0x00600060u;
+  p.t2_a = __builtin_amdgcn_perm(t, t, 0x01000100u);
+  p.t2_b = __builtin_amdgcn_perm(t, t, 0x03020302u);
+  p.t2n_a = p.t2_a | 0x80008000u;
+  p.t2n_b = p.t2_b | 0x80008000u;
+  p.scale_a = __uint_as_float((t << 16) - 0x04000000u);
+  p.scale_b = __uint_as_float((t & 0xFFFF0000u) - 0x04000000u);
+  return p;
+}
+
+__device__ __forceinline__ uint32_t fast_quant4(uint32_t x01, uint32_t x23, uint32_t t2, uint32_t t2n,
+                                                float scale) {
+  return cvt4_e4m3(clamp_mag2(x01, t2, t2n), clamp_mag2(x23, t2, t2n), scale);
+}
+
+// dim0 of a lane's 16 rows.  rm[i/2] = [row max of row i, row i+1] over the
+// lane's 8 columns; after two DPP moves, the quad's block amax.  Codes: 8 per
+// lane per row (one 256-byte segment per half-wave); one scale byte per quad.
 template <bool SPECIAL>
-__device__ __forceinline__ void dim0_rows(const uint2 (&d)[kWaveRows], int lane, uint8_t* __restrict__ q0,
-                                          uint8_t* __restrict__ s0, int64_t cols, int64_t sb_cols) {
+__device__ __forceinline__ void dim0_rows(const uint4 (&d)[kLaneRows], const uint32_t (&rm)[kLaneRows / 2],
+                                          bool quad_leader, __amdgpu_buffer_rsrc_t q0, int q0_off,
+                                          __amdgpu_buffer_rsrc_t s0, int s0_off, uint32_t cols,
+                                          uint32_t sb_cols) {
 #pragma unroll
-  for (int i = 0; i < kWaveRows; i += 2) {
-    uint32_t ma = max2(mag2(d[i].x), mag2(d[i].y));
-    uint32_t mb = max2(mag2(d[i + 1].x), mag2(d[i + 1].y));
-    uint32_t m = max2(__builtin_amdgcn_perm(mb, ma, 0x05040100u),   // [ma.lo, mb.lo]
-                      __builtin_amdgcn_perm(mb, ma, 0x07060302u));  // [ma.hi, mb.hi]
+  for (int i = 0; i < kLaneRows; i += 2) {
+    uint32_t m = rm[i / 2];
     m = max2(m, quad_swap1(m));
     m = max2(m, quad_swap2(m));
-    m = max2(m, half_row_mirror(m));
-    BlockParams pa = block_params<SPECIAL>(m & 0xFFFFu);
-    BlockParams pb = block_params<SPECIAL>(m >> 16);
-    *reinterpret_cast<uint32_t*>(q0 + (int64_t)i * cols) = quant4<SPECIAL>(d[i].x, d[i].y, pa);
-    *reinterpret_cast<uint32_t*>(q0 + (int64_t)(i + 1) * cols) = quant4<SPECIAL>(d[i + 1].x, d[i + 1].y, pb);
-    if ((lane & 7) == 0) {
-      s0[(int64_t)i * sb_cols] = (uint8_t)pa.byte;
-      s0[(int64_t)(i + 1) * sb_cols] = (uint8_t)pb.byte;
+    uint32_t qa0, qa1, qb0, qb1, ba, bb;
+    if (SPECIAL) {
+      BlockParams pa = block_params<true>(m & 0xFFFFu);
+      BlockParams pb = block_params<true>(m >> 16);
+      qa0 = quant4<true>(d[i].x, d[i].y, pa);
+      qa1 = quant4<true>(d[i].z, d[i].w, pa);
+      qb0 = quant4<true>(d[i + 1].x, d[i + 1].y, pb);
+      qb1 = quant4<true>(d[i + 1].z, d[i + 1].w, pb);
+      ba = pa.byte;
+      bb = pb.byte;
+    } else {
+      const PairParams p = pair_params(m);
+      qa0 = fast_quant4(d[i].x, d[i].y, p.t2_a, p.t2n_a, p.scale_a);
+      qa1 = fast_quant4(d[i].z, d[i].w, p.t2_a, p.t2n_a, p.scale_a);
+      qb0 = fast_quant4(d[i + 1].x, d[i + 1].y, p.t2_b, p.t2n_b, p.scale_b);
+      qb1 = fast_quant4(d[i + 1].z, d[i + 1].w, p.t2_b, p.t2n_b, p.scale_b);
+      ba = __float_as_uint(p.scale_a) >> 23;
+      bb = __float_as_uint(p.scale_b) >> 23;
+    }
+    __builtin_amdgcn_raw_buffer_store_b64((u32x2){qa0, qa1}, q0, q0_off, (int)(i * cols), 0);
+    __builtin_amdgcn_raw_buffer_store_b64((u32x2){qb0, qb1}, q0, q0_off, (int)((i + 1) * cols), 0);
+    if (quad_leader) {
+      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)ba, s0, s0_off, (int)(i * sb_cols), 0);
+      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)bb, s0, s0_off, (int)((i + 1) * sb_cols), 0);
     }
   }
 }
 
-// dim1 of a wave's 32 rows: for each of the lane's 4 columns, 32 codes into
-// two LDS slots and the scale byte into the column's scale word.
+// dim1 of a lane's 16 rows: for each of its 8 columns, 16 codes into one LDS
+// slot; the lower half-wave also records the column's scale byte.
 template <bool SPECIAL>
-__device__ __forceinline__ void dim1_rows(const uint2 (&d)[kWaveRows], const uint32_t (&cm)[2], int lane,
-                                          int wave, uint4* q1_lds, uint8_t* s1_lds) {
+__device__ __forceinline__ void dim1_cols(const uint4 (&d)[kLaneRows], const uint32_t (&cm)[4], int lc,
+                                          int slot, bool lower, uint4* q1_lds, uint8_t* s1_lds, int wave) {
 #pragma unroll
-  for (int j = 0; j < kLaneCols; ++j) {
-    const int k = j >> 1;
-    const bool hi = j & 1;
-    BlockParams p = block_params<SPECIAL>(hi ? (cm[k] >> 16) : (cm[k] & 0xFFFFu));
-    const uint32_t sel = hi ? 0x07060302u : 0x05040100u;
-    uint32_t w[8];
-#pragma unroll
-    for (int i = 0; i < kWaveRows; i += 4) {
-      // Column j of rows (i, i+1) and (i+2, i+3) as bf16 pairs.
-      uint32_t p01 = __builtin_amdgcn_perm(half_of(d[i + 1], k), half_of(d[i], k), sel);
-      uint32_t p23 = __builtin_amdgcn_perm(half_of(d[i + 3], k), half_of(d[i + 2], k), sel);
-      w[i / 4] = quant4<SPECIAL>(p01, p23, p);
+  for (int k = 0; k < 4; ++k) {
+    uint32_t t2[2], t2n[2], bytes[2];
+    float scale[2];
+    BlockParams bp[2];
+    if (SPECIAL) {
+      bp[0] = block_params<true>(cm[k] & 0xFFFFu);
+      bp[1] = block_params<true>(cm[k] >> 16);
+      bytes[0] = bp[0].byte;
+      bytes[1] = bp[1].byte;
+    } else {
+      const PairParams p = pair_params(cm[k]);
+      t2[0] = p.t2_a;
+      t2n[0] = p.t2n_a;
+      scale[0] = p.scale_a;
+      t2[1] = p.t2_b;
+      t2n[1] = p.t2n_b;
+      scale[1] = p.scale_b;
+      bytes[0] = __float_as_uint(p.scale_a) >> 23;
+      bytes[1] = __float_as_uint(p.scale_b) >> 23;
     }
-    const int col = lane * kLaneCols + j;
-    q1_lds[q1_slot(col, 2 * wave)] = make_uint4(w[0], w[1], w[2], w[3]);
-    q1_lds[q1_slot(col, 2 * wave + 1)] = make_uint4(w[4], w[5], w[6], w[7]);
-    s1_lds[col * kWaves + wave] = (uint8_t)p.byte;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t sel = h ? 0x07060302u : 0x05040100u;
+      uint32_t w[4];
+#pragma unroll
+      for (int i = 0; i < kLaneRows; i += 4) {
+        // Column 2k+h of rows (i, i+1) and (i+2, i+3) as bf16 pairs.
+        uint32_t p01 = __builtin_amdgcn_perm(word(d[i + 1], k), word(d[i], k), sel);
+        uint32_t p23 = __builtin_amdgcn_perm(word(d[i + 3], k), word(d[i + 2], k), sel);
+        w[i / 4] = SPECIAL ? quant4<true>(p01, p23, bp[h]) : fast_quant4(p01, p23, t2[h], t2n[h], scale[h]);
+      }
+      const int col = lc * kLaneCols + 2 * k + h;
+      q1_lds[q1_slot(col, slot)] = make_uint4(w[0], w[1], w[2], w[3]);
+      if (lower)
+        s1_lds[col * kWaves + wave] = (uint8_t)bytes[h];
+    }
   }
 }
 
-// Tile order: groups of kRowGroup row tiles; inside a group, column tiles
+struct CastArgs {
+  const uint16_t* x;
+  int64_t rows, cols, rows_per_seg;
+  uint32_t row_tiles, col_tiles, walks, per_xcd;
+  uint8_t *q0, *s0, *q1, *s1;
+};
+
+struct Stage {
+  uint4 q1[kTileCols * kSlots];   // dim1 codes, 128 rows x 256 columns
+  uint32_t s1[kTileCols];         // dim1 scale bytes, 4 blocks per column
+};
+struct NoStage {};
+
+// Work order: groups of kRowGroup row bands; inside a group, column walks
 // outermost; each XCD takes a contiguous run of this order.
-__device__ __forceinline__ bool tile_of(uint32_t bid, uint32_t row_tiles, uint32_t col_tiles,
-                                        uint32_t per_xcd, uint32_t& rt, uint32_t& ct) {
+__device__ __forceinline__ bool work_of(uint32_t bid, uint32_t row_tiles, uint32_t walks,
+                                        uint32_t per_xcd, uint32_t& rt, uint32_t& cw) {
   const uint32_t id = (bid % kXcds) * per_xcd + bid / kXcds;
-  if (id >= row_tiles * col_tiles)
+  if (id >= row_tiles * walks)
     return false;
-  const uint32_t group_tiles = kRowGroup * col_tiles;
-  const uint32_t g = id / group_tiles;
-  const uint32_t within = id - g * group_tiles;
+  const uint32_t group_items = kRowGroup * walks;
+  const uint32_t g = id / group_items;
+  const uint32_t within = id - g * group_items;
   const uint32_t gs = min((uint32_t)kRowGroup, row_tiles - g * kRowGroup);
-  ct = within / gs;
-  rt = g * kRowGroup + (within - ct * gs);
+  cw = within / gs;
+  rt = g * kRowGroup + (within - cw * gs);
   return true;
 }
 
@@ -136,145 +199,234 @@ __device__ __forceinline__ bool tile_of(uint32_t bid, uint32_t row_tiles, uint32
 // a (cols, rows_per_seg) matrix at e * cols * rows_per_seg, its scales a
 // (cols, rows_per_seg / 32) matrix at e * cols * rows_per_seg / 32.
 template <bool DIM0, bool DIM1>
-__global__ __launch_bounds__(256) void cast_kernel(const uint16_t* __restrict__ x, int64_t rows,
-                                                   int64_t cols, int64_t rows_per_seg,
-                                                   uint32_t row_tiles, uint32_t col_tiles,
-                                                   uint32_t per_xcd, uint8_t* __restrict__ q0,
-                                                   uint8_t* __restrict__ s0,
-                                                   uint8_t* __restrict__ q1,
-                                                   uint8_t* __restrict__ s1) {
-  __shared__ uint4 q1_lds[DIM1 ? kTileCols * kSlots : 1];
-  __shared__ uint8_t s1_lds[DIM1 ? kTileCols * kWaves : 1];
+__global__ __launch_bounds__(256) void cast_kernel(CastArgs a) {
+  __shared__ std::conditional_t<DIM1, Stage, NoStage> stage[2];
 
-  uint32_t rt, ct;
-  if (!tile_of(blockIdx.x, row_tiles, col_tiles, per_xcd, rt, ct))
+  uint32_t rt, cw;
+  if (!work_of(blockIdx.x, a.row_tiles, a.walks, a.per_xcd, rt, cw))
     return;  // uniform over the workgroup
-  const int wave = threadIdx.x >> 6;
+  // The wave index is uniform; saying so keeps the buffer descriptors built
+  // from it in scalar registers.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
+  const int half = lane >> 5;      // which 16 rows of the wave's 32
+  const int lc = lane & 31;        // which 8 columns of the tile
+  const int64_t cols = a.cols;
   const int64_t tile_r = (int64_t)rt * kTileRows;
-  const int64_t tile_c = (int64_t)ct * kTileCols;
   const int64_t r0 = tile_r + wave * kWaveRows;
-  const int64_t c = tile_c + lane * kLaneCols;
-  // rows, cols are multiples of 32: a wave is fully in or out, and the 8
-  // lanes of a dim0 block agree.
-  const bool on = r0 < rows && c < cols;
+  // rows and cols are multiples of 32: a wave is fully in or out, and the 4
+  // lanes of a dim0 block agree.  Waves below the last row load the band's
+  // first rows instead (never used), so that every wave issues every load.
+  const bool wave_on = r0 < a.rows;
+  const int64_t r_load = wave_on ? r0 : tile_r;
+  const uint32_t ct0 = cw * kWalk;
+  const int steps = (int)min((uint32_t)kWalk, a.col_tiles - ct0);
+  const uint32_t row_bytes = (uint32_t)(cols * 2);
 
-  if (on) {
-    uint2 d[kWaveRows];
-    const uint16_t* src = x + r0 * cols + c;
+  auto tile_c = [&](int s) -> int64_t { return (int64_t)(ct0 + s) * kTileCols; };
+  // Row i of this lane is row r0 + 16 * half + i; lanes past the last column
+  // reread the first column of their rows (never stored).
+  auto load = [&](uint4 (&d)[kLaneRows], int s) {
+    const bool col_on = tile_c(s) + lc * kLaneCols < cols;
+    const int x_off = (int)(half * kLaneRows * row_bytes) + (col_on ? lc * 16 : 0);
+    const __amdgpu_buffer_rsrc_t xs = buffer_rsrc(a.x + r_load * cols + tile_c(s), 0xFFFFFFFFu);
 #pragma unroll
-    for (int i = 0; i < kWaveRows; ++i)
-      d[i] = *reinterpret_cast<const uint2*>(src + (int64_t)i * cols);
-
-    uint32_t cm[2];
-    column_max(d, cm);
-    const uint32_t all = max2(cm[0], cm[1]);
-    const bool special = (all & 0xFFFFu) >= kInfBits || (all >> 16) >= kInfBits;
-    // Any +-Inf or NaN among the wave's active lanes sends the wave down the
-    // general path (uniform branch); finite data never pays for it.
-    const bool any_special = __any(special);
-    if (DIM1) {
-      if (any_special)
-        dim1_rows<true>(d, cm, lane, wave, q1_lds, s1_lds);
-      else
-        dim1_rows<false>(d, cm, lane, wave, q1_lds, s1_lds);
+    for (int i = 0; i < kLaneRows; ++i) {
+      auto v = __builtin_amdgcn_raw_buffer_load_b128(xs, x_off, (int)(i * row_bytes), 0);
+      d[i] = make_uint4(v[0], v[1], v[2], v[3]);
     }
-    if (DIM0) {
-      uint8_t* q0_row = q0 + r0 * cols + c;
-      uint8_t* s0_row = s0 + r0 * (cols / 32) + c / 32;
-      if (any_special)
-        dim0_rows<true>(d, lane, q0_row, s0_row, cols, cols / 32);
-      else
-        dim0_rows<false>(d, lane, q0_row, s0_row, cols, cols / 32);
-    }
-  }
+  };
 
-  if (DIM1) {
-    __syncthreads();
-    const int valid_rows = (int)min((int64_t)kTileRows, rows - tile_r);   // multiple of 32
-    const int valid_cols = (int)min((int64_t)kTileCols, cols - tile_c);
-    // Segment of the tile's first row; the tile crosses at most a few
-    // segment ends (segments are multiples of 32 rows).
-    const int64_t seg0 = tile_r / rows_per_seg;
-    const int64_t off0 = tile_r - seg0 * rows_per_seg;
-    const bool one_seg = off0 + valid_rows <= rows_per_seg;
-    const int64_t seg_blocks = rows_per_seg / 32;
-
-    // Codes: 8 lanes per column, 16 bytes each; a wave covers 8 columns per pass.
-    const int slot = threadIdx.x & 7;
-#pragma unroll 4
-    for (int pass = 0; pass < kTileCols / 32; ++pass) {
-      const int col = pass * 32 + (threadIdx.x >> 3);
-      if (col < valid_cols && slot * 16 < valid_rows) {
-        int64_t seg = seg0, off = off0 + slot * 16;
-        while (off >= rows_per_seg) {
-          off -= rows_per_seg;
-          ++seg;
+  auto process = [&](const uint4 (&d)[kLaneRows], int s) {
+    const int64_t tc = tile_c(s);
+    const bool on = wave_on && tc + lc * kLaneCols < cols;
+    if (wave_on) {
+      // Magnitudes once; row maxima of row pairs and column maxima from them.
+      uint32_t rm[kLaneRows / 2];
+      uint32_t cm[4];
+      {
+        uint32_t mg[kLaneRows][4];
+#pragma unroll
+        for (int i = 0; i < kLaneRows; ++i) {
+          mg[i][0] = mag2(d[i].x);
+          mg[i][1] = mag2(d[i].y);
+          mg[i][2] = mag2(d[i].z);
+          mg[i][3] = mag2(d[i].w);
         }
-        uint8_t* dst = q1 + (seg * cols + tile_c + col) * rows_per_seg + off;
-        *reinterpret_cast<uint4*>(dst) = q1_lds[q1_slot(col, slot)];
+#pragma unroll
+        for (int i = 0; i < kLaneRows; i += 2) {
+          const uint32_t ma = max2(max2(mg[i][0], mg[i][1]), max2(mg[i][2], mg[i][3]));
+          const uint32_t mb = max2(max2(mg[i + 1][0], mg[i + 1][1]), max2(mg[i + 1][2], mg[i + 1][3]));
+          rm[i / 2] = max2(__builtin_amdgcn_perm(mb, ma, 0x05040100u),   // [ma.lo, mb.lo]
+                           __builtin_amdgcn_perm(mb, ma, 0x07060302u));  // [ma.hi, mb.hi]
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          uint32_t t[kLaneRows / 2];
+#pragma unroll
+          for (int i = 0; i < kLaneRows / 2; ++i)
+            t[i] = max2(mg[2 * i][k], mg[2 * i + 1][k]);
+#pragma unroll
+          for (int w = kLaneRows / 4; w >= 1; w >>= 1)
+#pragma unroll
+            for (int i = 0; i < w; ++i)
+              t[i] = max2(t[i], t[i + w]);
+          // combine with the partner lane holding the other 16 rows
+          auto sw = __builtin_amdgcn_permlane32_swap(t[0], t[0], false, false);
+          cm[k] = max2(sw[0], sw[1]);
+        }
+      }
+      const uint32_t all = max2(max2(cm[0], cm[1]), max2(cm[2], cm[3]));
+      const bool special = on && ((all & 0xFFFFu) >= kInfBits || (all >> 16) >= kInfBits);
+      // Any +-Inf or NaN among the wave's lanes sends the wave down the
+      // general path (uniform branch); finite data never pays for it.
+      const bool any_special = __any(special);
+      if (on) {
+        if constexpr (DIM1) {
+          const int slot = 2 * wave + half;
+          uint8_t* s1b = reinterpret_cast<uint8_t*>(stage[s & 1].s1);
+          if (any_special)
+            dim1_cols<true>(d, cm, lc, slot, half == 0, stage[s & 1].q1, s1b, wave);
+          else
+            dim1_cols<false>(d, cm, lc, slot, half == 0, stage[s & 1].q1, s1b, wave);
+        }
+        if constexpr (DIM0) {
+          const uint32_t sb = (uint32_t)(cols / 32);
+          const __amdgpu_buffer_rsrc_t q0 = buffer_rsrc(a.q0 + r0 * cols + tc, 0xFFFFFFFFu);
+          const __amdgpu_buffer_rsrc_t s0 = buffer_rsrc(a.s0 + r0 * (cols / 32) + tc / 32, 0xFFFFFFFFu);
+          const int q0_off = (int)(half * kLaneRows * (uint32_t)cols) + lc * kLaneCols;
+          const int s0_off = (int)(half * kLaneRows * sb) + (lc >> 2);
+          const bool leader = (lc & 3) == 0;
+          if (any_special)
+            dim0_rows<true>(d, rm, leader, q0, q0_off, s0, s0_off, (uint32_t)cols, sb);
+          else
+            dim0_rows<false>(d, rm, leader, q0, q0_off, s0, s0_off, (uint32_t)cols, sb);
+        }
       }
     }
-    // Scales: one thread per column, the four 32-row blocks of the tile.
-    const int col = threadIdx.x;
-    if (col < valid_cols) {
-      const uint32_t v = reinterpret_cast<const uint32_t*>(s1_lds)[col];
-      const int nblk = valid_rows / 32;
-      uint8_t* dst = s1 + (seg0 * cols + tile_c + col) * seg_blocks + off0 / 32;
-      if (one_seg && nblk == kWaves && ((uintptr_t)dst % 4) == 0) {
-        *reinterpret_cast<uint32_t*>(dst) = v;
-      } else {
-        for (int b = 0; b < nblk; ++b) {
-          int64_t seg = seg0, off = off0 + 32 * b;
-          while (off >= rows_per_seg) {
-            off -= rows_per_seg;
+
+    if constexpr (DIM1) {
+      // Two stages alternate, so one barrier per tile keeps a wave from
+      // overwriting a stage that another wave is still storing.
+      lds_barrier();
+      const Stage& st = stage[s & 1];
+      const int valid_rows = (int)min((int64_t)kTileRows, a.rows - tile_r);   // multiple of 32
+      const int valid_cols = (int)min((int64_t)kTileCols, cols - tc);
+      const int64_t rps = a.rows_per_seg;
+      // Segment of the band's first row; the band crosses at most a few
+      // segment ends (segments are multiples of 32 rows).
+      const int64_t seg0 = tile_r / rps;
+      const int64_t off0 = tile_r - seg0 * rps;
+      const bool one_seg = off0 + valid_rows <= rps;
+      const int64_t seg_blocks = rps / 32;
+      // Codes: 8 lanes per column, 16 bytes each; a wave covers 8 columns per pass.
+      const int slot = threadIdx.x & 7;
+#pragma unroll 4
+      for (int pass = 0; pass < kTileCols / 32; ++pass) {
+        const int col = pass * 32 + (threadIdx.x >> 3);
+        if (col < valid_cols && slot * 16 < valid_rows) {
+          int64_t seg = seg0, off = off0 + slot * 16;
+          while (off >= rps) {
+            off -= rps;
             ++seg;
           }
-          s1[(seg * cols + tile_c + col) * seg_blocks + off / 32] = (uint8_t)(v >> (8 * b));
+          uint8_t* dst = a.q1 + (seg * cols + tc + col) * rps + off;
+          *reinterpret_cast<uint4*>(dst) = st.q1[q1_slot(col, slot)];
+        }
+      }
+      // Scales: one thread per column, the four 32-row blocks of the band.
+      const int col = threadIdx.x;
+      if (col < valid_cols) {
+        const uint32_t v = st.s1[col];
+        const int nblk = valid_rows / 32;
+        uint8_t* dst = a.s1 + (seg0 * cols + tc + col) * seg_blocks + off0 / 32;
+        if (one_seg && nblk == kWaves && ((uintptr_t)dst % 4) == 0) {
+          *reinterpret_cast<uint32_t*>(dst) = v;
+        } else {
+          for (int b = 0; b < nblk; ++b) {
+            int64_t seg = seg0, off = off0 + 32 * b;
+            while (off >= rps) {
+              off -= rps;
+              ++seg;
+            }
+            a.s1[(seg * cols + tc + col) * seg_blocks + off / 32] = (uint8_t)(v >> (8 * b));
+          }
         }
       }
     }
+  };
+
+  // Two register buffers alternate: while one tile is processed, the next one
+  // is loading.  Inside the loop every prefetch is unconditional, so the wait
+  // before a tile covers only that tile's loads; the scheduling barriers keep
+  // the compiler from sinking a prefetch below the work on the other buffer.
+  uint4 buf_a[kLaneRows], buf_b[kLaneRows];
+  load(buf_a, 0);
+  int s = 0;
+  for (; s + 2 < steps; s += 2) {
+    load(buf_b, s + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    process(buf_a, s);
+    load(buf_a, s + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    process(buf_b, s + 1);
+  }
+  if (s + 2 == steps) {
+    load(buf_b, s + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    process(buf_a, s);
+    process(buf_b, s + 1);
+  } else {
+    process(buf_a, s);
   }
 }
 
-struct CastGrid {
-  uint32_t row_tiles, col_tiles, per_xcd;
-  int64_t blocks;
-};
-
-static CastGrid cast_grid(int64_t rows, int64_t cols) {
-  CastGrid g;
+static CastArgs cast_args(const uint16_t* x, int64_t rows, int64_t cols, int64_t rows_per_seg,
+                          uint8_t* q0, uint8_t* s0, uint8_t* q1, uint8_t* s1, int64_t* blocks) {
+  CastArgs a;
+  a.x = x;
+  a.rows = rows;
+  a.cols = cols;
+  a.rows_per_seg = rows_per_seg;
+  a.q0 = q0;
+  a.s0 = s0;
+  a.q1 = q1;
+  a.s1 = s1;
   const int64_t rt = (rows + kTileRows - 1) / kTileRows;
   const int64_t ct = (cols + kTileCols - 1) / kTileCols;
-  const int64_t per = (rt * ct + kXcds - 1) / kXcds;
-  g.row_tiles = (uint32_t)rt;
-  g.col_tiles = (uint32_t)ct;
-  g.per_xcd = (uint32_t)per;
-  g.blocks = per * kXcds;
-  return g;
+  const int64_t walks = (ct + kWalk - 1) / kWalk;
+  const int64_t per = (rt * walks + kXcds - 1) / kXcds;
+  a.row_tiles = (uint32_t)rt;
+  a.col_tiles = (uint32_t)ct;
+  a.walks = (uint32_t)walks;
+  a.per_xcd = (uint32_t)per;
+  *blocks = per * kXcds;
+  return a;
 }
 
-int64_t cast_grid_blocks(int64_t rows, int64_t cols) { return cast_grid(rows, cols).blocks; }
+int64_t cast_grid_blocks(int64_t rows, int64_t cols) {
+  int64_t blocks;
+  cast_args(nullptr, rows, cols, rows, nullptr, nullptr, nullptr, nullptr, &blocks);
+  return blocks;
+}
 
 template <bool DIM0, bool DIM1>
-static hipError_t launch_cast(const uint16_t* x, int64_t rows, int64_t cols, int64_t rows_per_seg,
-                              uint8_t* q0, uint8_t* s0, uint8_t* q1, uint8_t* s1,
-                              hipStream_t stream) {
-  const CastGrid g = cast_grid(rows, cols);
-  hipLaunchKernelGGL((cast_kernel<DIM0, DIM1>), dim3((unsigned)g.blocks), dim3(kWaves * 64), 0, stream,
-                     x, rows, cols, rows_per_seg, g.row_tiles, g.col_tiles, g.per_xcd, q0, s0, q1, s1);
+static hipError_t launch_cast(const CastArgs& a, int64_t blocks, hipStream_t stream) {
+  hipLaunchKernelGGL((cast_kernel<DIM0, DIM1>), dim3((unsigned)blocks), dim3(kWaves * 64), 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_cast_any(const uint16_t* x, int64_t rows, int64_t cols, int64_t rows_per_seg,
                            uint8_t* q0, uint8_t* s0, uint8_t* q1, uint8_t* s1,
                            hipStream_t stream) {
+  int64_t blocks;
+  const CastArgs a = cast_args(x, rows, cols, rows_per_seg, q0, s0, q1, s1, &blocks);
   const bool d0 = q0 != nullptr, d1 = q1 != nullptr;
   if (d0 && d1)
-    return launch_cast<true, true>(x, rows, cols, rows_per_seg, q0, s0, q1, s1, stream);
+    return launch_cast<true, true>(a, blocks, stream);
   if (d0)
-    return launch_cast<true, false>(x, rows, cols, rows_per_seg, q0, s0, q1, s1, stream);
-  return launch_cast<false, true>(x, rows, cols, rows_per_seg, q0, s0, q1, s1, stream);
+    return launch_cast<true, false>(a, blocks, stream);
+  return launch_cast<false, true>(a, blocks, stream);
 }
 
 }  // namespace mx

@@ -25,6 +25,15 @@ __device__ __forceinline__ uint32_t as_u32(u16x2 v) { return __builtin_bit_cast(
 __device__ __forceinline__ i16x2 as_i16x2(uint32_t v) { return __builtin_bit_cast(i16x2, v); }
 __device__ __forceinline__ uint32_t as_u32(i16x2 v) { return __builtin_bit_cast(uint32_t, v); }
 
+// Workgroup barrier that orders LDS only.  __syncthreads() is a full
+// workgroup fence and waits for every outstanding global load too, which
+// would drain the loads a wave has prefetched for its next tile.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Raw buffer resource over [base, base + bytes) for buffer loads and stores
 // whose row offset sits in a scalar register (no per-lane address math).
 // The third descriptor word is the gfx950 raw-buffer format.
