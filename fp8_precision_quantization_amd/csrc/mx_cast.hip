@@ -8,21 +8,28 @@
 //   wave      = 32 rows x 256 columns, one dim1 block height: lanes 0-31 hold
 //               rows 0-15 and lanes 32-63 rows 16-31 of the same columns;
 //   lane      = 16 rows x 8 columns, loaded as 16 x 16-byte row segments.
-// Each load instruction of a wave reads two 512-byte row segments.  A dim0
-// block (32 columns of one row) spans a quad of lanes and is reduced with two
-// DPP moves; a dim1 block (32 rows of one column) is split between lanes l and
-// l + 32: an in-lane tree of packed 16-bit maxes, then one permlane32 swap.
-// The magnitudes are formed once and feed both reductions.
+// Each load instruction of a wave reads two 512-byte row segments; loads and
+// row-major stores are buffer instructions whose row offset sits in a scalar
+// register, and the input loads are non-temporal.  A dim0 block (32 columns
+// of one row) spans a quad of lanes and is reduced with two DPP moves; a dim1
+// block (32 rows of one column) is split between lanes l and l + 32: an
+// in-lane tree of packed 16-bit maxes, then one permlane32 swap.  The
+// magnitudes are formed once for both.
 //
 // Stores are shaped for the memory system rather than for the lanes that
 // produce them.  dim0 codes leave each wave as 256-byte row segments.  The
 // dim1 codes of a column (16 bytes per lane) are staged in LDS, and once the
 // four waves are done the workgroup writes each column's 128 rows as one full
 // 128-byte line, eight lanes x 16 bytes per line; dim1 scale bytes are staged
-// the same way and leave as one 4-byte run per column.  Workgroups are
-// numbered so that the 32 tiles of one column range that share the lines of
-// the dim1 scale matrix run back to back on the same XCD (workgroups are
-// dispatched round-robin over the 8 XCDs), where that XCD's L2 merges them.
+// the same way and leave as one 4-byte run per column.  The barrier between
+// the two orders LDS only: __syncthreads() would also wait for global memory.
+//
+// Workgroups are numbered so that each XCD (workgroups are dispatched
+// round-robin over the 8 XCDs) works on a compact region of the matrix:
+// row_group row tiles side by side, column tiles outermost.  Its L2 then
+// merges the partial lines of the scale matrices, and the region's shape
+// sets how long the contiguous runs of reads and stores are.  The shape and
+// the non-temporal loads were chosen by timing on MI355X.
 #include <type_traits>
 
 #include "mx_device.h"
@@ -38,9 +45,10 @@ constexpr int kTileRows = kWaves * kWaveRows;   // 128
 constexpr int kLaneCols = 8;
 constexpr int kTileCols = 32 * kLaneCols;       // 256
 constexpr int kXcds = 8;
-constexpr int kRowGroup = 32;                   // row tiles sharing one dim1 scale line
-constexpr int kWalk = 8;                        // tiles per workgroup along the columns
 constexpr int kSlots = kTileRows / 16;          // 16-byte slots per staged column (8)
+constexpr int kLoadNT = 2;                      // cache-policy bits of the input loads: nt
+constexpr uint32_t kRowGroupBoth = 4;           // see cast_args
+constexpr uint32_t kRowGroupDim1 = 128;
 
 __device__ __forceinline__ uint32_t word(const uint4& v, int k) {
   return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
@@ -168,7 +176,8 @@ __device__ __forceinline__ void dim1_cols(const uint4 (&d)[kLaneRows], const uin
 struct CastArgs {
   const uint16_t* x;
   int64_t rows, cols, rows_per_seg;
-  uint32_t row_tiles, col_tiles, walks, per_xcd;
+  uint32_t row_tiles, col_tiles, per_xcd;
+  uint32_t row_group;  // row bands that run side by side on one XCD
   uint8_t *q0, *s0, *q1, *s1;
 };
 
@@ -176,21 +185,22 @@ struct Stage {
   uint4 q1[kTileCols * kSlots];   // dim1 codes, 128 rows x 256 columns
   uint32_t s1[kTileCols];         // dim1 scale bytes, 4 blocks per column
 };
-struct NoStage {};
+struct NoStage {};  // dim0-only casts stage nothing
 
-// Work order: groups of kRowGroup row bands; inside a group, column walks
+// Work order: groups of row_group row tiles; inside a group, column tiles
 // outermost; each XCD takes a contiguous run of this order.
-__device__ __forceinline__ bool work_of(uint32_t bid, uint32_t row_tiles, uint32_t walks,
-                                        uint32_t per_xcd, uint32_t& rt, uint32_t& cw) {
+__device__ __forceinline__ bool tile_of(uint32_t bid, uint32_t row_tiles, uint32_t col_tiles,
+                                        uint32_t per_xcd, uint32_t row_group, uint32_t& rt,
+                                        uint32_t& ct) {
   const uint32_t id = (bid % kXcds) * per_xcd + bid / kXcds;
-  if (id >= row_tiles * walks)
+  if (id >= row_tiles * col_tiles)
     return false;
-  const uint32_t group_items = kRowGroup * walks;
+  const uint32_t group_items = row_group * col_tiles;
   const uint32_t g = id / group_items;
   const uint32_t within = id - g * group_items;
-  const uint32_t gs = min((uint32_t)kRowGroup, row_tiles - g * kRowGroup);
-  cw = within / gs;
-  rt = g * kRowGroup + (within - cw * gs);
+  const uint32_t gs = min(row_group, row_tiles - g * row_group);
+  ct = within / gs;
+  rt = g * row_group + (within - ct * gs);
   return true;
 }
 
@@ -200,10 +210,10 @@ __device__ __forceinline__ bool work_of(uint32_t bid, uint32_t row_tiles, uint32
 // (cols, rows_per_seg / 32) matrix at e * cols * rows_per_seg / 32.
 template <bool DIM0, bool DIM1>
 __global__ __launch_bounds__(256) void cast_kernel(CastArgs a) {
-  __shared__ std::conditional_t<DIM1, Stage, NoStage> stage[2];
+  __shared__ std::conditional_t<DIM1, Stage, NoStage> stage;
 
-  uint32_t rt, cw;
-  if (!work_of(blockIdx.x, a.row_tiles, a.walks, a.per_xcd, rt, cw))
+  uint32_t rt, ct;
+  if (!tile_of(blockIdx.x, a.row_tiles, a.col_tiles, a.per_xcd, a.row_group, rt, ct))
     return;  // uniform over the workgroup
   // The wave index is uniform; saying so keeps the buffer descriptors built
   // from it in scalar registers.
@@ -214,33 +224,26 @@ __global__ __launch_bounds__(256) void cast_kernel(CastArgs a) {
   const int64_t cols = a.cols;
   const int64_t tile_r = (int64_t)rt * kTileRows;
   const int64_t r0 = tile_r + wave * kWaveRows;
+  const int64_t tc = (int64_t)ct * kTileCols;
   // rows and cols are multiples of 32: a wave is fully in or out, and the 4
-  // lanes of a dim0 block agree.  Waves below the last row load the band's
-  // first rows instead (never used), so that every wave issues every load.
+  // lanes of a dim0 block agree.
   const bool wave_on = r0 < a.rows;
-  const int64_t r_load = wave_on ? r0 : tile_r;
-  const uint32_t ct0 = cw * kWalk;
-  const int steps = (int)min((uint32_t)kWalk, a.col_tiles - ct0);
-  const uint32_t row_bytes = (uint32_t)(cols * 2);
+  const bool on = wave_on && tc + lc * kLaneCols < cols;
 
-  auto tile_c = [&](int s) -> int64_t { return (int64_t)(ct0 + s) * kTileCols; };
-  // Row i of this lane is row r0 + 16 * half + i; lanes past the last column
-  // reread the first column of their rows (never stored).
-  auto load = [&](uint4 (&d)[kLaneRows], int s) {
-    const bool col_on = tile_c(s) + lc * kLaneCols < cols;
-    const int x_off = (int)(half * kLaneRows * row_bytes) + (col_on ? lc * 16 : 0);
-    const __amdgpu_buffer_rsrc_t xs = buffer_rsrc(a.x + r_load * cols + tile_c(s), 0xFFFFFFFFu);
+  if (wave_on) {
+    // Row i of this lane is row r0 + 16 * half + i; lanes past the last
+    // column reread the first column of their rows (never stored).
+    const uint32_t row_bytes = (uint32_t)(cols * 2);
+    const int x_off = (int)(half * kLaneRows * row_bytes) + (on ? lc * 16 : 0);
+    const __amdgpu_buffer_rsrc_t xs = buffer_rsrc(a.x + r0 * cols + tc, 0xFFFFFFFFu);
+    uint4 d[kLaneRows];
 #pragma unroll
     for (int i = 0; i < kLaneRows; ++i) {
-      auto v = __builtin_amdgcn_raw_buffer_load_b128(xs, x_off, (int)(i * row_bytes), 0);
+      // non-temporal: the input is read once
+      auto v = __builtin_amdgcn_raw_buffer_load_b128(xs, x_off, (int)(i * row_bytes), kLoadNT);
       d[i] = make_uint4(v[0], v[1], v[2], v[3]);
     }
-  };
-
-  auto process = [&](const uint4 (&d)[kLaneRows], int s) {
-    const int64_t tc = tile_c(s);
-    const bool on = wave_on && tc + lc * kLaneCols < cols;
-    if (wave_on) {
+    {
       // Magnitudes once; row maxima of row pairs and column maxima from them.
       uint32_t rm[kLaneRows / 2];
       uint32_t cm[4];
@@ -284,11 +287,11 @@ __global__ __launch_bounds__(256) void cast_kernel(CastArgs a) {
       if (on) {
         if constexpr (DIM1) {
           const int slot = 2 * wave + half;
-          uint8_t* s1b = reinterpret_cast<uint8_t*>(stage[s & 1].s1);
+          uint8_t* s1b = reinterpret_cast<uint8_t*>(stage.s1);
           if (any_special)
-            dim1_cols<true>(d, cm, lc, slot, half == 0, stage[s & 1].q1, s1b, wave);
+            dim1_cols<true>(d, cm, lc, slot, half == 0, stage.q1, s1b, wave);
           else
-            dim1_cols<false>(d, cm, lc, slot, half == 0, stage[s & 1].q1, s1b, wave);
+            dim1_cols<false>(d, cm, lc, slot, half == 0, stage.q1, s1b, wave);
         }
         if constexpr (DIM0) {
           const uint32_t sb = (uint32_t)(cols / 32);
@@ -304,80 +307,56 @@ __global__ __launch_bounds__(256) void cast_kernel(CastArgs a) {
         }
       }
     }
+  }
 
-    if constexpr (DIM1) {
-      // Two stages alternate, so one barrier per tile keeps a wave from
-      // overwriting a stage that another wave is still storing.
-      lds_barrier();
-      const Stage& st = stage[s & 1];
-      const int valid_rows = (int)min((int64_t)kTileRows, a.rows - tile_r);   // multiple of 32
-      const int valid_cols = (int)min((int64_t)kTileCols, cols - tc);
-      const int64_t rps = a.rows_per_seg;
-      // Segment of the band's first row; the band crosses at most a few
-      // segment ends (segments are multiples of 32 rows).
-      const int64_t seg0 = tile_r / rps;
-      const int64_t off0 = tile_r - seg0 * rps;
-      const bool one_seg = off0 + valid_rows <= rps;
-      const int64_t seg_blocks = rps / 32;
-      // Codes: 8 lanes per column, 16 bytes each; a wave covers 8 columns per pass.
-      const int slot = threadIdx.x & 7;
+  if constexpr (DIM1) {
+    // Every wave reaches the barrier; it orders LDS only (no wait on
+    // global memory).
+    lds_barrier();
+    const Stage& st = stage;
+    const int valid_rows = (int)min((int64_t)kTileRows, a.rows - tile_r);   // multiple of 32
+    const int valid_cols = (int)min((int64_t)kTileCols, cols - tc);
+    const int64_t rps = a.rows_per_seg;
+    // Segment of the band's first row; the band crosses at most a few
+    // segment ends (segments are multiples of 32 rows).
+    const int64_t seg0 = tile_r / rps;
+    const int64_t off0 = tile_r - seg0 * rps;
+    const bool one_seg = off0 + valid_rows <= rps;
+    const int64_t seg_blocks = rps / 32;
+    // Codes: 8 lanes per column, 16 bytes each; a wave covers 8 columns per pass.
+    const int slot = threadIdx.x & 7;
 #pragma unroll 4
-      for (int pass = 0; pass < kTileCols / 32; ++pass) {
-        const int col = pass * 32 + (threadIdx.x >> 3);
-        if (col < valid_cols && slot * 16 < valid_rows) {
-          int64_t seg = seg0, off = off0 + slot * 16;
+    for (int pass = 0; pass < kTileCols / 32; ++pass) {
+      const int col = pass * 32 + (threadIdx.x >> 3);
+      if (col < valid_cols && slot * 16 < valid_rows) {
+        int64_t seg = seg0, off = off0 + slot * 16;
+        while (off >= rps) {
+          off -= rps;
+          ++seg;
+        }
+        uint8_t* dst = a.q1 + (seg * cols + tc + col) * rps + off;
+        *reinterpret_cast<uint4*>(dst) = st.q1[q1_slot(col, slot)];
+      }
+    }
+    // Scales: one thread per column, the four 32-row blocks of the band.
+    const int col = threadIdx.x;
+    if (col < valid_cols) {
+      const uint32_t v = st.s1[col];
+      const int nblk = valid_rows / 32;
+      uint8_t* dst = a.s1 + (seg0 * cols + tc + col) * seg_blocks + off0 / 32;
+      if (one_seg && nblk == kWaves && ((uintptr_t)dst % 4) == 0) {
+        *reinterpret_cast<uint32_t*>(dst) = v;
+      } else {
+        for (int b = 0; b < nblk; ++b) {
+          int64_t seg = seg0, off = off0 + 32 * b;
           while (off >= rps) {
             off -= rps;
             ++seg;
           }
-          uint8_t* dst = a.q1 + (seg * cols + tc + col) * rps + off;
-          *reinterpret_cast<uint4*>(dst) = st.q1[q1_slot(col, slot)];
-        }
-      }
-      // Scales: one thread per column, the four 32-row blocks of the band.
-      const int col = threadIdx.x;
-      if (col < valid_cols) {
-        const uint32_t v = st.s1[col];
-        const int nblk = valid_rows / 32;
-        uint8_t* dst = a.s1 + (seg0 * cols + tc + col) * seg_blocks + off0 / 32;
-        if (one_seg && nblk == kWaves && ((uintptr_t)dst % 4) == 0) {
-          *reinterpret_cast<uint32_t*>(dst) = v;
-        } else {
-          for (int b = 0; b < nblk; ++b) {
-            int64_t seg = seg0, off = off0 + 32 * b;
-            while (off >= rps) {
-              off -= rps;
-              ++seg;
-            }
-            a.s1[(seg * cols + tc + col) * seg_blocks + off / 32] = (uint8_t)(v >> (8 * b));
-          }
+          a.s1[(seg * cols + tc + col) * seg_blocks + off / 32] = (uint8_t)(v >> (8 * b));
         }
       }
     }
-  };
-
-  // Two register buffers alternate: while one tile is processed, the next one
-  // is loading.  Inside the loop every prefetch is unconditional, so the wait
-  // before a tile covers only that tile's loads; the scheduling barriers keep
-  // the compiler from sinking a prefetch below the work on the other buffer.
-  uint4 buf_a[kLaneRows], buf_b[kLaneRows];
-  load(buf_a, 0);
-  int s = 0;
-  for (; s + 2 < steps; s += 2) {
-    load(buf_b, s + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    process(buf_a, s);
-    load(buf_a, s + 2);
-    __builtin_amdgcn_sched_barrier(0);
-    process(buf_b, s + 1);
-  }
-  if (s + 2 == steps) {
-    load(buf_b, s + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    process(buf_a, s);
-    process(buf_b, s + 1);
-  } else {
-    process(buf_a, s);
   }
 }
 
@@ -394,12 +373,14 @@ static CastArgs cast_args(const uint16_t* x, int64_t rows, int64_t cols, int64_t
   a.s1 = s1;
   const int64_t rt = (rows + kTileRows - 1) / kTileRows;
   const int64_t ct = (cols + kTileCols - 1) / kTileCols;
-  const int64_t walks = (ct + kWalk - 1) / kWalk;
-  const int64_t per = (rt * walks + kXcds - 1) / kXcds;
+  const int64_t per = (rt * ct + kXcds - 1) / kXcds;
   a.row_tiles = (uint32_t)rt;
   a.col_tiles = (uint32_t)ct;
-  a.walks = (uint32_t)walks;
   a.per_xcd = (uint32_t)per;
+  // Bands per XCD group, chosen by timing on MI355X: the dim0+dim1 cast
+  // favours wide groups (its row-major reads and stores dominate), the
+  // dim1-only cast tall ones (all of its stores are col-major).
+  a.row_group = q0 != nullptr ? kRowGroupBoth : kRowGroupDim1;
   *blocks = per * kXcds;
   return a;
 }
