@@ -4,8 +4,11 @@
 
 One step is one pass of the hot path over one batch of synthetic input held
 in HBM.  The default workload is the headline one: the bf16 -> MXFP8 dim0 +
-dim1 cast of a 16384 x 16384 matrix with heavy-tailed rows, followed by the
-128x4 blocked layout of both scale sets.  Other workloads (for profiling):
+dim1 cast of a 16384 x 16384 matrix with heavy-tailed rows, with both scale
+sets written in the 128x4 blocked layout by the same launch.  Other workloads
+(for profiling):
+  square16384_3launch  the same result from three launches: the cast with
+             plain scales, then mx_scales_to_blocked on each scale set;
   moe16640   cast of (16640, 5120) activations + M-grouped layout of the row
              scales (4 groups along M, offsets on the device);
   kgroups    K-grouped layouts of (5120, 512), (8192, 4096), (2048, 4096)
@@ -114,25 +117,37 @@ class Timer:
 # --------------------------------------------------------------------------
 # workloads
 # --------------------------------------------------------------------------
-def setup_square(dev, n=16384):
+def setup_square(dev, n=16384, fused=True):
     log("generating %dx%d heavy-tailed bf16 input" % (n, n))
     bits = workloads.heavy_tailed_rows(n, n, seed=2)
     x = to_dev_bf16(bits, dev)
     q0 = torch.empty((n, n), dtype=torch.uint8, device=dev)
-    s0 = torch.empty((n, n // 32), dtype=torch.uint8, device=dev)
     q1 = torch.empty((n, n), dtype=torch.uint8, device=dev)
-    s1 = torch.empty((n, n // 32), dtype=torch.uint8, device=dev)
     b0 = torch.empty((pad(n, 128), pad(n // 32, 4)), dtype=torch.uint8, device=dev)
     b1 = torch.empty_like(b0)
     timer = Timer()
+    if fused:
+        def step():
+            with timer:
+                mx.mx_cast_dim0_dim1_blocked(x, out=(q0, b0, q1, b1), raw=True)
 
-    def step():
-        with timer:
-            mx.mx_cast_dim0_dim1(x, out=(q0, s0, q1, s1), raw=True)
-        mx.mx_scales_to_blocked(s0, out=b0, raw=True)
-        mx.mx_scales_to_blocked(s1, out=b1, raw=True)
+        # one launch reads X and writes both codes and both blocked scale sets
+        kern_bytes = 4 * n * n + 2 * pad(n, 128) * pad(n // 32, 4)
+        step_bytes = kern_bytes
+        kern_name = "cast dim0+dim1, blocked scales"
+    else:
+        s0 = torch.empty((n, n // 32), dtype=torch.uint8, device=dev)
+        s1 = torch.empty((n, n // 32), dtype=torch.uint8, device=dev)
 
-    step_bytes = cast_bytes(n, n) + 2 * blocked_bytes(n, n // 32)
+        def step():
+            with timer:
+                mx.mx_cast_dim0_dim1(x, out=(q0, s0, q1, s1), raw=True)
+            mx.mx_scales_to_blocked(s0, out=b0, raw=True)
+            mx.mx_scales_to_blocked(s1, out=b1, raw=True)
+
+        kern_bytes = cast_bytes(n, n)
+        step_bytes = cast_bytes(n, n) + 2 * blocked_bytes(n, n // 32)
+        kern_name = "cast dim0+dim1"
 
     def cpu_baseline():
         import oracle
@@ -141,24 +156,33 @@ def setup_square(dev, n=16384):
         t0 = time.perf_counter()
         r_q0, r_s0 = oracle.cast_dim0(sample)
         r_q1, r_s1 = oracle.cast_dim1(sample)
-        oracle.to_blocked(r_s0)
-        oracle.to_blocked(r_s1)
+        r_b0 = oracle.to_blocked(r_s0)
+        r_b1 = oracle.to_blocked(r_s1)
         dt = time.perf_counter() - t0
-        nbytes = cast_bytes(rows, n) + blocked_bytes(rows, n // 32) + blocked_bytes(n, rows // 32)
+        nbytes = 4 * rows * n + r_b0.size + r_b1.size
+        # the sample's row scales are the first rows/128 row tiles of b0; its
+        # column scales are the first rows/128 column tiles of every row tile of b1
+        g_b1 = b1.view(pad(n, 128) // 128, pad(n // 32, 4) // 4, 512)[:, :rows // 128]
         ok = (np.array_equal(q0[:rows].cpu().numpy(), r_q0)
-              and np.array_equal(s0[:rows].cpu().numpy(), r_s0)
               and np.array_equal(q1[:, :rows].cpu().numpy(), r_q1)
-              and np.array_equal(s1[:, :rows // 32].cpu().numpy(), r_s1))
+              and np.array_equal(b0[:rows].cpu().numpy().reshape(-1), r_b0)
+              and np.array_equal(g_b1.cpu().numpy().reshape(-1), r_b1))
         return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
                 "kind": "oracle",
-                "sample": "rows 0..%d of the %dx%d input (dim0+dim1 cast + blocked layout of "
-                          "both scale sets), %.1f s wall" % (rows, n, n, dt),
+                "sample": "rows 0..%d of the %dx%d input (dim0+dim1 cast, both scale sets in the "
+                          "blocked layout), %.1f s wall" % (rows, n, n, dt),
                 "matches_gpu": bool(ok)}
 
-    config = {"workload": "mx_cast_dim0_dim1 %dx%d bf16 (heavy-tailed rows) + blocked "
-                          "layout of both scale sets" % (n, n),
+    config = {"workload": "mx_cast_dim0_dim1%s %dx%d bf16 (heavy-tailed rows), both scale sets "
+                          "in the 128x4 blocked layout%s"
+                          % ("_blocked" if fused else "", n, n,
+                             "" if fused else " by two mx_scales_to_blocked launches"),
               "rows": n, "cols": n, "block": 32, "elem": "e4m3", "scale": "e8m0"}
-    return step, step_bytes, timer, cast_bytes(n, n), "cast dim0+dim1", cpu_baseline, config
+    return step, step_bytes, timer, kern_bytes, kern_name, cpu_baseline, config
+
+
+def setup_square_3launch(dev):
+    return setup_square(dev, fused=False)
 
 
 def setup_moe(dev):
@@ -248,7 +272,8 @@ def setup_copy(dev, nbytes=1 << 30):
     return step, 2 * nbytes, timer, 2 * nbytes, "copy", None, config
 
 
-WORKLOADS = {"square16384": setup_square, "moe16640": setup_moe, "kgroups": setup_kgroups,
+WORKLOADS = {"square16384": setup_square, "square16384_3launch": setup_square_3launch,
+             "moe16640": setup_moe, "kgroups": setup_kgroups,
              "experts16": setup_experts, "copy": setup_copy}
 
 

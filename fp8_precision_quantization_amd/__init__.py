@@ -11,7 +11,9 @@ from ._binding import (  # noqa: F401
     mx_blocked_bytes,
     mx_blocked_grouped_bytes,
     mx_cast_dim0_dim1,
+    mx_cast_dim0_dim1_blocked,
     mx_cast_dim1_3d,
+    mx_cast_dim1_3d_blocked,
     mx_scales_to_blocked,
     mx_scales_to_blocked_grouped,
     status_string,

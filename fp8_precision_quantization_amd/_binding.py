@@ -31,6 +31,8 @@ SIGNATURES = {
     "mx_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "mx_cast_dim0_dim1": ([_vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "mx_cast_dim1_3d": ([_vp, _i64, _i64, _i64, _vp, _vp, _vp], ctypes.c_int),
+    "mx_cast_dim0_dim1_blocked": ([_vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
+    "mx_cast_dim1_3d_blocked": ([_vp, _i64, _i64, _i64, _vp, _vp, _vp], ctypes.c_int),
     "mx_blocked_bytes": ([_i64, _i64, _i64], _i64),
     "mx_scales_to_blocked": ([_vp, _i64, _i64, _i64, _vp, _vp], ctypes.c_int),
     "mx_blocked_grouped_bytes": ([_i64, _i64, _i32, _i32], _i64),
@@ -104,6 +106,10 @@ def _bf16_input(x, ndim, name):
         raise ValueError("%s must be contiguous" % name)
 
 
+def _pad(v, m):
+    return (v + m - 1) // m * m
+
+
 def _views(q, s, raw):
     if raw:
         return q, s
@@ -143,6 +149,38 @@ def mx_cast_dim1_3d(w, out=None, raw: bool = False):
     return _views(q, s, raw)
 
 
+def mx_cast_dim0_dim1_blocked(x, dim0: bool = True, dim1: bool = True, out=None, raw: bool = False):
+    """As mx_cast_dim0_dim1, with both scale sets written directly in the
+    128x4 blocked layout: s_row as (ceil128(R), ceil4(C/32)) and s_col as
+    (ceil128(C), ceil4(R/32)), padding 0."""
+    _bf16_input(x, 2, "x")
+    rows, cols = x.shape
+    o = out if out is not None else (None, None, None, None)
+    q0 = _out(o[0], (rows, cols), x.device, "q_row") if dim0 else None
+    s0 = _out(o[1], (_pad(rows, 128), _pad(cols // MX_BLOCK, 4)), x.device, "s_row_blocked") if dim0 else None
+    q1 = _out(o[2], (cols, rows), x.device, "q_col") if dim1 else None
+    s1 = _out(o[3], (_pad(cols, 128), _pad(rows // MX_BLOCK, 4)), x.device, "s_col_blocked") if dim1 else None
+    _check(lib().mx_cast_dim0_dim1_blocked(_ptr(x), rows, cols, _ptr(q0), _ptr(s0), _ptr(q1), _ptr(s1),
+                                           _stream(x.device)), "mx_cast_dim0_dim1_blocked")
+    r0 = _views(q0, s0, raw) if dim0 else (None, None)
+    r1 = _views(q1, s1, raw) if dim1 else (None, None)
+    return r0[0], r0[1], r1[0], r1[1]
+
+
+def mx_cast_dim1_3d_blocked(w, out=None, raw: bool = False):
+    """bf16 (E, N, K) -> (q (E, K, N), s (E, ceil128(K), ceil4(N/32))): the
+    per-expert dim1 cast with each expert's scales in the blocked layout.
+    N must be a multiple of 128."""
+    _bf16_input(w, 3, "w")
+    e, n, k = w.shape
+    o = out if out is not None else (None, None)
+    q = _out(o[0], (e, k, n), w.device, "q")
+    s = _out(o[1], (e, _pad(k, 128), _pad(n // MX_BLOCK, 4)), w.device, "s_blocked")
+    _check(lib().mx_cast_dim1_3d_blocked(_ptr(w), e, n, k, _ptr(q), _ptr(s), _stream(w.device)),
+           "mx_cast_dim1_3d_blocked")
+    return _views(q, s, raw)
+
+
 def mx_blocked_bytes(batch: int, rows: int, cols: int) -> int:
     return lib().mx_blocked_bytes(batch, rows, cols)
 
@@ -158,10 +196,6 @@ def _scale_input(s, name="scales"):
     if not s.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
     return s
-
-
-def _pad(v, m):
-    return (v + m - 1) // m * m
 
 
 def mx_scales_to_blocked(s, out=None, raw: bool = False):

@@ -54,7 +54,33 @@ mx_status mx_cast_dim0_dim1(const void* x, int64_t rows, int64_t cols, uint8_t* 
     return MX_ERR_ALIGN;
   return from_hip(mx::launch_cast_any(static_cast<const uint16_t*>(x), rows, cols, rows,
                                       d0 ? q_row : nullptr, d0 ? s_row : nullptr,
-                                      d1 ? q_col : nullptr, d1 ? s_col : nullptr, stream));
+                                      d1 ? q_col : nullptr, d1 ? s_col : nullptr, false, stream));
+}
+
+mx_status mx_cast_dim0_dim1_blocked(const void* x, int64_t rows, int64_t cols, uint8_t* q_row,
+                                    uint8_t* s_row_blocked, uint8_t* q_col, uint8_t* s_col_blocked,
+                                    hipStream_t stream) {
+  if (rows < 0 || cols < 0 || rows % MX_BLOCK != 0 || cols % MX_BLOCK != 0 || rows > kMaxExtent ||
+      cols > kMaxCastCols)
+    return MX_ERR_SHAPE;
+  if (rows == 0 || cols == 0)
+    return MX_OK;  // nothing to read or write; the pointers may be NULL
+  const bool d0 = q_row != nullptr || s_row_blocked != nullptr;
+  const bool d1 = q_col != nullptr || s_col_blocked != nullptr;
+  if (x == nullptr || (!d0 && !d1))
+    return MX_ERR_NULL;
+  if ((d0 && (q_row == nullptr || s_row_blocked == nullptr)) ||
+      (d1 && (q_col == nullptr || s_col_blocked == nullptr)))
+    return MX_ERR_NULL;
+  if (mx::cast_grid_blocks(rows, cols) > kMaxGridBlocks)
+    return MX_ERR_SHAPE;
+  if (!aligned(x, 16) || (d0 && (!aligned(q_row, 8) || !aligned(s_row_blocked, 16))) ||
+      (d1 && (!aligned(q_col, 16) || !aligned(s_col_blocked, 16))))
+    return MX_ERR_ALIGN;
+  return from_hip(mx::launch_cast_any(static_cast<const uint16_t*>(x), rows, cols, rows,
+                                      d0 ? q_row : nullptr, d0 ? s_row_blocked : nullptr,
+                                      d1 ? q_col : nullptr, d1 ? s_col_blocked : nullptr, true,
+                                      stream));
 }
 
 mx_status mx_cast_dim1_3d(const void* w, int64_t experts, int64_t n, int64_t k, uint8_t* q,
@@ -72,7 +98,25 @@ mx_status mx_cast_dim1_3d(const void* w, int64_t experts, int64_t n, int64_t k, 
   if (!aligned(w, 16) || !aligned(q, 16))
     return MX_ERR_ALIGN;
   return from_hip(mx::launch_cast_any(static_cast<const uint16_t*>(w), experts * n, k, n, nullptr,
-                                      nullptr, q, s, stream));
+                                      nullptr, q, s, false, stream));
+}
+
+mx_status mx_cast_dim1_3d_blocked(const void* w, int64_t experts, int64_t n, int64_t k, uint8_t* q,
+                                  uint8_t* s_blocked, hipStream_t stream) {
+  if (experts < 0 || n < 0 || k < 0 || n % 128 != 0 || k % MX_BLOCK != 0 ||
+      experts > kMaxExtent || n > kMaxExtent || k > kMaxCastCols ||
+      (n > 0 && experts > kMaxExtent / n))
+    return MX_ERR_SHAPE;
+  if (experts == 0 || n == 0 || k == 0)
+    return MX_OK;  // nothing to read or write; the pointers may be NULL
+  if (w == nullptr || q == nullptr || s_blocked == nullptr)
+    return MX_ERR_NULL;
+  if (mx::cast_grid_blocks(experts * n, k) > kMaxGridBlocks)
+    return MX_ERR_SHAPE;
+  if (!aligned(w, 16) || !aligned(q, 16) || !aligned(s_blocked, 16))
+    return MX_ERR_ALIGN;
+  return from_hip(mx::launch_cast_any(static_cast<const uint16_t*>(w), experts * n, k, n, nullptr,
+                                      nullptr, q, s_blocked, true, stream));
 }
 
 int64_t mx_blocked_bytes(int64_t batch, int64_t rows, int64_t cols) {

@@ -24,6 +24,14 @@
 // the same way and leave as one 4-byte run per column.  The barrier between
 // the two orders LDS only: __syncthreads() would also wait for global memory.
 //
+// With BLK the scales come out directly in the 128x4 blocked layout that
+// grouped GEMMs read (pytorch/ao issue "[mxfp8 moe training] add compile
+// support", the to_blocked layout of the scale tensors): a tile of 128 rows
+// and 256 columns owns two 512-byte blocks of dim0 scales (128 rows x 4
+// scale columns each) and two of dim1 scales (128 columns x 4 row blocks),
+// so each is assembled in LDS and stored as whole 16-byte chunks, the
+// padding bytes of a ragged edge written as zero by the tile that owns them.
+//
 // Workgroups are numbered so that each XCD (workgroups are dispatched
 // round-robin over the 8 XCDs) works on a compact region of the matrix:
 // row_group row tiles side by side, column tiles outermost.  Its L2 then
@@ -89,12 +97,14 @@ __device__ __forceinline__ uint32_t fast_quant4(uint32_t x01, uint32_t x23, uint
 
 // dim0 of a lane's 16 rows.  rm[i/2] = [row max of row i, row i+1] over the
 // lane's 8 columns; after two DPP moves, the quad's block amax.  Codes: 8 per
-// lane per row (one 256-byte segment per half-wave); one scale byte per quad.
-template <bool SPECIAL>
+// lane per row (one 256-byte segment per half-wave).  Scale bytes (one per
+// quad): straight to the plain scale matrix, or (BLK) into the LDS image of
+// the tile's two 128x4 blocked tiles at s0_lds + blk_off.
+template <bool SPECIAL, bool BLK>
 __device__ __forceinline__ void dim0_rows(const uint4 (&d)[kLaneRows], const uint32_t (&rm)[kLaneRows / 2],
                                           bool quad_leader, __amdgpu_buffer_rsrc_t q0, int q0_off,
                                           __amdgpu_buffer_rsrc_t s0, int s0_off, uint32_t cols,
-                                          uint32_t sb_cols) {
+                                          uint32_t sb_cols, uint8_t* s0_lds, int blk_off) {
 #pragma unroll
   for (int i = 0; i < kLaneRows; i += 2) {
     uint32_t m = rm[i / 2];
@@ -122,10 +132,28 @@ __device__ __forceinline__ void dim0_rows(const uint4 (&d)[kLaneRows], const uin
     __builtin_amdgcn_raw_buffer_store_b64((u32x2){qa0, qa1}, q0, q0_off, (int)(i * cols), 0);
     __builtin_amdgcn_raw_buffer_store_b64((u32x2){qb0, qb1}, q0, q0_off, (int)((i + 1) * cols), 0);
     if (quad_leader) {
-      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)ba, s0, s0_off, (int)(i * sb_cols), 0);
-      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)bb, s0, s0_off, (int)((i + 1) * sb_cols), 0);
+      if (BLK) {
+        // rows i, i+1 of the lane are consecutive rows inside a 32-row sub-block
+        s0_lds[blk_off + i * 16] = (uint8_t)ba;
+        s0_lds[blk_off + (i + 1) * 16] = (uint8_t)bb;
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)ba, s0, s0_off, (int)(i * sb_cols), 0);
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)bb, s0, s0_off, (int)((i + 1) * sb_cols), 0);
+      }
     }
   }
+}
+
+// One 16-byte chunk of a 128x4 blocked tile: tile row i (0..31) holds rows
+// i, 32+i, 64+i, 96+i (4 bytes each, columns 0..3).  Bytes of rows at or past
+// valid_blocks * 32 and of columns at or past valid_cols become 0.
+__device__ __forceinline__ uint4 mask_chunk(uint4 v, int valid_blocks, int valid_cols) {
+  const uint32_t cmask = valid_cols >= 4 ? 0xFFFFFFFFu : valid_cols <= 0 ? 0u : (1u << (8 * valid_cols)) - 1u;
+  v.x = valid_blocks > 0 ? v.x & cmask : 0u;
+  v.y = valid_blocks > 1 ? v.y & cmask : 0u;
+  v.z = valid_blocks > 2 ? v.z & cmask : 0u;
+  v.w = valid_blocks > 3 ? v.w & cmask : 0u;
+  return v;
 }
 
 // dim1 of a lane's 16 rows: for each of its 8 columns, 16 codes into one LDS
@@ -178,6 +206,9 @@ struct CastArgs {
   int64_t rows, cols, rows_per_seg;
   uint32_t row_tiles, col_tiles, per_xcd;
   uint32_t row_group;  // row bands that run side by side on one XCD
+  // Blocked scale outputs: column blocks of the dim0 scale matrix, of one
+  // segment's dim1 scale matrix, and that matrix's size in bytes.
+  int64_t ncb0, ncb1, seg_blk_bytes;
   uint8_t *q0, *s0, *q1, *s1;
 };
 
@@ -208,9 +239,15 @@ __device__ __forceinline__ bool tile_of(uint32_t bid, uint32_t row_tiles, uint32
 // (3D weights: one per expert; 2D: one segment).  Segment e's dim1 output is
 // a (cols, rows_per_seg) matrix at e * cols * rows_per_seg, its scales a
 // (cols, rows_per_seg / 32) matrix at e * cols * rows_per_seg / 32.
-template <bool DIM0, bool DIM1>
+// BLK: the scale outputs are written in the 128x4 blocked layout instead of
+// plain row-major matrices.  A tile's dim0 scales are exactly two whole
+// blocked tiles (its 128 rows x 8 scale columns) and its dim1 scales two more
+// (256 matrix rows x 4 scale columns), so every blocked tile, padding
+// included, is written by exactly one workgroup.
+template <bool DIM0, bool DIM1, bool BLK>
 __global__ __launch_bounds__(256) void cast_kernel(CastArgs a) {
   __shared__ std::conditional_t<DIM1, Stage, NoStage> stage;
+  __shared__ uint8_t s0_blk[(DIM0 && BLK) ? 2 * 512 : 1];
 
   uint32_t rt, ct;
   if (!tile_of(blockIdx.x, a.row_tiles, a.col_tiles, a.per_xcd, a.row_group, rt, ct))
@@ -300,22 +337,39 @@ __global__ __launch_bounds__(256) void cast_kernel(CastArgs a) {
           const int q0_off = (int)(half * kLaneRows * (uint32_t)cols) + lc * kLaneCols;
           const int s0_off = (int)(half * kLaneRows * sb) + (lc >> 2);
           const bool leader = (lc & 3) == 0;
+          // blocked image: tile (lc >> 4), row 16 * half + i of sub-block
+          // `wave`, column (lc >> 2) & 3
+          const int blk_off = (lc >> 4) * 512 + half * 256 + wave * 4 + ((lc >> 2) & 3);
           if (any_special)
-            dim0_rows<true>(d, rm, leader, q0, q0_off, s0, s0_off, (uint32_t)cols, sb);
+            dim0_rows<true, BLK>(d, rm, leader, q0, q0_off, s0, s0_off, (uint32_t)cols, sb, s0_blk, blk_off);
           else
-            dim0_rows<false>(d, rm, leader, q0, q0_off, s0, s0_off, (uint32_t)cols, sb);
+            dim0_rows<false, BLK>(d, rm, leader, q0, q0_off, s0, s0_off, (uint32_t)cols, sb, s0_blk, blk_off);
         }
       }
     }
   }
 
-  if constexpr (DIM1) {
+  if constexpr (DIM1 || (DIM0 && BLK)) {
     // Every wave reaches the barrier; it orders LDS only (no wait on
     // global memory).
     lds_barrier();
+  }
+  const int valid_rows = (int)min((int64_t)kTileRows, a.rows - tile_r);   // multiple of 32
+  const int valid_cols = (int)min((int64_t)kTileCols, cols - tc);
+  if constexpr (DIM0 && BLK) {
+    // Two blocked tiles (scale columns 8 ct .. 8 ct + 7), 32 chunks each.
+    if (wave == 0) {
+      const int t = lane >> 5, i = lane & 31;
+      const int64_t cb = 2 * (int64_t)ct + t;
+      if (cb < a.ncb0) {
+        uint4 v = reinterpret_cast<const uint4*>(s0_blk)[t * 32 + i];
+        v = mask_chunk(v, valid_rows / 32, (int)min((int64_t)4, cols / 32 - 4 * cb));
+        *reinterpret_cast<uint4*>(a.s0 + ((int64_t)rt * a.ncb0 + cb) * 512 + i * 16) = v;
+      }
+    }
+  }
+  if constexpr (DIM1) {
     const Stage& st = stage;
-    const int valid_rows = (int)min((int64_t)kTileRows, a.rows - tile_r);   // multiple of 32
-    const int valid_cols = (int)min((int64_t)kTileCols, cols - tc);
     const int64_t rps = a.rows_per_seg;
     // Segment of the band's first row; the band crosses at most a few
     // segment ends (segments are multiples of 32 rows).
@@ -338,22 +392,42 @@ __global__ __launch_bounds__(256) void cast_kernel(CastArgs a) {
         *reinterpret_cast<uint4*>(dst) = st.q1[q1_slot(col, slot)];
       }
     }
-    // Scales: one thread per column, the four 32-row blocks of the band.
-    const int col = threadIdx.x;
-    if (col < valid_cols) {
-      const uint32_t v = st.s1[col];
-      const int nblk = valid_rows / 32;
-      uint8_t* dst = a.s1 + (seg0 * cols + tc + col) * seg_blocks + off0 / 32;
-      if (one_seg && nblk == kWaves && ((uintptr_t)dst % 4) == 0) {
-        *reinterpret_cast<uint32_t*>(dst) = v;
-      } else {
-        for (int b = 0; b < nblk; ++b) {
-          int64_t seg = seg0, off = off0 + 32 * b;
-          while (off >= rps) {
-            off -= rps;
-            ++seg;
+    if constexpr (BLK) {
+      // Two blocked tiles of the segment's dim1 scale matrix: matrix rows
+      // (x columns) tc .. tc + 255, scale column block off0 / 128 (the host
+      // guarantees that a tile never crosses a segment end here).  Chunk i of
+      // tile t holds columns 128 t + 32 s + i, s = 0..3, 4 row blocks each.
+      if (wave == 1) {
+        const int t = lane >> 5, i = lane & 31;
+        const int64_t rb = 2 * (int64_t)ct + t;
+        if (rb * 128 < cols) {
+          uint4 v = make_uint4(st.s1[128 * t + i], st.s1[128 * t + 32 + i], st.s1[128 * t + 64 + i],
+                               st.s1[128 * t + 96 + i]);
+          const int64_t left = cols - (tc + 128 * t + i);   // columns from this one on
+          const int valid_s = (int)min((int64_t)4, max((int64_t)0, (left + 31) / 32));
+          v = mask_chunk(v, valid_s, valid_rows / 32);
+          *reinterpret_cast<uint4*>(a.s1 + seg0 * a.seg_blk_bytes + (rb * a.ncb1 + off0 / 128) * 512 +
+                                    i * 16) = v;
+        }
+      }
+    } else {
+      // Plain scales: one thread per column, the four 32-row blocks of the band.
+      const int col = threadIdx.x;
+      if (col < valid_cols) {
+        const uint32_t v = st.s1[col];
+        const int nblk = valid_rows / 32;
+        uint8_t* dst = a.s1 + (seg0 * cols + tc + col) * seg_blocks + off0 / 32;
+        if (one_seg && nblk == kWaves && ((uintptr_t)dst % 4) == 0) {
+          *reinterpret_cast<uint32_t*>(dst) = v;
+        } else {
+          for (int b = 0; b < nblk; ++b) {
+            int64_t seg = seg0, off = off0 + 32 * b;
+            while (off >= rps) {
+              off -= rps;
+              ++seg;
+            }
+            a.s1[(seg * cols + tc + col) * seg_blocks + off / 32] = (uint8_t)(v >> (8 * b));
           }
-          a.s1[(seg * cols + tc + col) * seg_blocks + off / 32] = (uint8_t)(v >> (8 * b));
         }
       }
     }
@@ -381,6 +455,9 @@ static CastArgs cast_args(const uint16_t* x, int64_t rows, int64_t cols, int64_t
   // favours wide groups (its row-major reads and stores dominate), the
   // dim1-only cast tall ones (all of its stores are col-major).
   a.row_group = q0 != nullptr ? kRowGroupBoth : kRowGroupDim1;
+  a.ncb0 = (cols / 32 + 3) / 4;
+  a.ncb1 = (rows_per_seg / 32 + 3) / 4;
+  a.seg_blk_bytes = (cols + 127) / 128 * 128 * (a.ncb1 * 4);
   *blocks = per * kXcds;
   return a;
 }
@@ -391,23 +468,30 @@ int64_t cast_grid_blocks(int64_t rows, int64_t cols) {
   return blocks;
 }
 
-template <bool DIM0, bool DIM1>
+template <bool DIM0, bool DIM1, bool BLK>
 static hipError_t launch_cast(const CastArgs& a, int64_t blocks, hipStream_t stream) {
-  hipLaunchKernelGGL((cast_kernel<DIM0, DIM1>), dim3((unsigned)blocks), dim3(kWaves * 64), 0, stream, a);
+  hipLaunchKernelGGL((cast_kernel<DIM0, DIM1, BLK>), dim3((unsigned)blocks), dim3(kWaves * 64), 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_cast_any(const uint16_t* x, int64_t rows, int64_t cols, int64_t rows_per_seg,
-                           uint8_t* q0, uint8_t* s0, uint8_t* q1, uint8_t* s1,
+                           uint8_t* q0, uint8_t* s0, uint8_t* q1, uint8_t* s1, bool blocked,
                            hipStream_t stream) {
   int64_t blocks;
   const CastArgs a = cast_args(x, rows, cols, rows_per_seg, q0, s0, q1, s1, &blocks);
   const bool d0 = q0 != nullptr, d1 = q1 != nullptr;
+  if (blocked) {
+    if (d0 && d1)
+      return launch_cast<true, true, true>(a, blocks, stream);
+    if (d0)
+      return launch_cast<true, false, true>(a, blocks, stream);
+    return launch_cast<false, true, true>(a, blocks, stream);
+  }
   if (d0 && d1)
-    return launch_cast<true, true>(a, blocks, stream);
+    return launch_cast<true, true, false>(a, blocks, stream);
   if (d0)
-    return launch_cast<true, false>(a, blocks, stream);
-  return launch_cast<false, true>(a, blocks, stream);
+    return launch_cast<true, false, false>(a, blocks, stream);
+  return launch_cast<false, true, false>(a, blocks, stream);
 }
 
 }  // namespace mx

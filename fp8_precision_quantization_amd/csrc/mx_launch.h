@@ -9,8 +9,10 @@ namespace mx {
 // Cast kernel: rows x cols bf16; q0/s0 (dim0) and/or q1/s1 (dim1) non-null.
 // rows_per_seg splits the rows into segments whose dim1 outputs are stored
 // one after another (3D expert weights); pass rows for a plain 2D cast.
+// blocked: scales in the 128x4 blocked layout (dim1 segments must then be
+// multiples of 128 rows, or the whole matrix).
 hipError_t launch_cast_any(const uint16_t* x, int64_t rows, int64_t cols, int64_t rows_per_seg,
-                           uint8_t* q0, uint8_t* s0, uint8_t* q1, uint8_t* s1,
+                           uint8_t* q0, uint8_t* s0, uint8_t* q1, uint8_t* s1, bool blocked,
                            hipStream_t stream);
 int64_t cast_grid_blocks(int64_t rows, int64_t cols);
 

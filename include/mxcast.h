@@ -96,6 +96,24 @@ MX_API mx_status mx_cast_dim0_dim1(const void* x, int64_t rows, int64_t cols,
                             hipStream_t stream);
 
 /*
+ * The same cast with both scale sets written directly in the 128x4 blocked
+ * layout ("triton kernel to cast to mx across dim0 and dim1", future
+ * improvement 2: write out swizzled scales), saving the separate layout
+ * pass and its traffic.
+ *   s_row_blocked  mx_blocked_bytes(1, rows, cols / 32) bytes: the blocked
+ *                  form of the (rows, cols / 32) row scales; 16-byte aligned.
+ *   s_col_blocked  mx_blocked_bytes(1, cols, rows / 32) bytes: the blocked
+ *                  form of the (cols, rows / 32) column scales; 16-byte
+ *                  aligned.
+ * Every byte of both buffers is written (padding 0).  Codes, arguments and
+ * errors as for mx_cast_dim0_dim1.
+ */
+MX_API mx_status mx_cast_dim0_dim1_blocked(const void* x, int64_t rows, int64_t cols,
+                                           uint8_t* q_row, uint8_t* s_row_blocked,
+                                           uint8_t* q_col, uint8_t* s_col_blocked,
+                                           hipStream_t stream);
+
+/*
  * dim1 cast of 3D expert weights, expert by expert.
  *   w  bf16 (experts, n, k) contiguous; 16-byte aligned.
  *   q  e4m3 (experts, k, n): expert e's (n, k) matrix cast in blocks of 32
@@ -107,6 +125,17 @@ MX_API mx_status mx_cast_dim0_dim1(const void* x, int64_t rows, int64_t cols,
  */
 MX_API mx_status mx_cast_dim1_3d(const void* w, int64_t experts, int64_t n, int64_t k,
                           uint8_t* q, uint8_t* s, hipStream_t stream);
+
+/*
+ * The 3D dim1 cast with each expert's (k, n / 32) scales written directly in
+ * the 128x4 blocked layout: s_blocked holds mx_blocked_bytes(experts, k,
+ * n / 32) bytes, expert e's blocked matrix at e * ceil128(k) * ceil4(n / 32);
+ * every byte written (padding 0); 16-byte aligned.  n must be a multiple of
+ * 128 (so that no 128-row tile of the reshape spans two experts), else
+ * MX_ERR_SHAPE: use mx_cast_dim1_3d then mx_scales_to_blocked.
+ */
+MX_API mx_status mx_cast_dim1_3d_blocked(const void* w, int64_t experts, int64_t n, int64_t k,
+                                         uint8_t* q, uint8_t* s_blocked, hipStream_t stream);
 
 /* Bytes of the blocked form of `batch` (rows, cols) matrices:
  * batch * ceil128(rows) * ceil4(cols); -1 on a negative argument. */

@@ -3,11 +3,12 @@ configuration the benchmark times, against the CPU oracle on the same seeded
 inputs (bytes, tolerance 0).
 
   1. 1024 x 1024 N(0,1) with zero / denormal / outlier tiles  (test_gpu_cast)
-  2. 16384 x 16384 heavy-tailed rows: dim0+dim1 cast + blocked scales, in full
+  2. 16384 x 16384 heavy-tailed rows: dim0+dim1 cast + blocked scales, both as
+     three launches and as the one fused launch, in full
   3. 16640 x 5120 MoE activations: cast + M-grouped scales (4 groups), in full
   4. K-grouped scale layouts of (5120, 512), (8192, 4096), (2048, 4096), in full
-  5. (16, 8192, 5120) expert weights: dim1 3D cast + per-expert blocked scales,
-     all experts on the GPU, three of them compared in full
+  5. (16, 8192, 5120) expert weights: dim1 3D cast + per-expert blocked scales
+     (separate and fused), all experts on the GPU, three compared in full
 """
 import numpy as np
 import pytest
@@ -31,17 +32,24 @@ def test_square_16384_heavy_tailed(oracle_mod):
     q0, s0, q1, s1 = mx.mx_cast_dim0_dim1(x, raw=True)
     b0 = mx.mx_scales_to_blocked(s0, raw=True)
     b1 = mx.mx_scales_to_blocked(s1, raw=True)
+    f_q0, f_b0, f_q1, f_b1 = mx.mx_cast_dim0_dim1_blocked(x, raw=True)
     torch.cuda.synchronize(dev)
     del x
     r_q0, r_s0 = oracle_mod.cast_dim0(bits)
+    r_b0 = oracle_mod.to_blocked(r_s0)
     assert_bytes_equal(host(s0), r_s0, "16384^2 s_row")
     assert_bytes_equal(host(q0), r_q0, "16384^2 q_row")
-    assert_bytes_equal(host(b0).reshape(-1), oracle_mod.to_blocked(r_s0), "16384^2 blocked s_row")
-    del r_q0, q0
+    assert_bytes_equal(host(b0).reshape(-1), r_b0, "16384^2 blocked s_row")
+    assert_bytes_equal(host(f_q0), r_q0, "16384^2 fused q_row")
+    assert_bytes_equal(host(f_b0).reshape(-1), r_b0, "16384^2 fused blocked s_row")
+    del r_q0, q0, f_q0
     r_q1, r_s1 = oracle_mod.cast_dim1(bits)
+    r_b1 = oracle_mod.to_blocked(r_s1)
     assert_bytes_equal(host(s1), r_s1, "16384^2 s_col")
     assert_bytes_equal(host(q1), r_q1, "16384^2 q_col")
-    assert_bytes_equal(host(b1).reshape(-1), oracle_mod.to_blocked(r_s1), "16384^2 blocked s_col")
+    assert_bytes_equal(host(b1).reshape(-1), r_b1, "16384^2 blocked s_col")
+    assert_bytes_equal(host(f_q1), r_q1, "16384^2 fused q_col")
+    assert_bytes_equal(host(f_b1).reshape(-1), r_b1, "16384^2 fused blocked s_col")
     # heavy-tailed rows spread the row scales over ~two dozen binades; column
     # blocks take the max over 32 rows and so sit in fewer, higher ones
     assert len(np.unique(r_s0)) >= 20 and len(np.unique(r_s1)) >= 10
@@ -95,6 +103,7 @@ def test_expert_weights_dim1_3d(oracle_mod):
             checked[i] = bits
     q, s = mx.mx_cast_dim1_3d(w, raw=True)
     blk = mx.mx_scales_to_blocked(s, raw=True)
+    f_q, f_blk = mx.mx_cast_dim1_3d_blocked(w, raw=True)
     torch.cuda.synchronize(dev)
     del w
     assert tuple(q.shape) == (e, k, n) and tuple(s.shape) == (e, k, n // 32)
@@ -103,4 +112,7 @@ def test_expert_weights_dim1_3d(oracle_mod):
         r_q, r_s = oracle_mod.cast_dim1(bits)
         assert_bytes_equal(host(q[i]), r_q, "expert %d q" % i)
         assert_bytes_equal(host(s[i]), r_s, "expert %d s" % i)
-        assert_bytes_equal(host(blk[i]).reshape(-1), oracle_mod.to_blocked(r_s), "expert %d blocked" % i)
+        r_b = oracle_mod.to_blocked(r_s)
+        assert_bytes_equal(host(blk[i]).reshape(-1), r_b, "expert %d blocked" % i)
+        assert_bytes_equal(host(f_q[i]), r_q, "expert %d fused q" % i)
+        assert_bytes_equal(host(f_blk[i]).reshape(-1), r_b, "expert %d fused blocked" % i)

@@ -32,7 +32,8 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert set(names) == {"mx_status_string", "mx_cast_dim0_dim1", "mx_cast_dim1_3d",
+    assert set(names) == {"mx_status_string", "mx_cast_dim0_dim1", "mx_cast_dim0_dim1_blocked",
+                          "mx_cast_dim1_3d", "mx_cast_dim1_3d_blocked",
                           "mx_blocked_bytes", "mx_scales_to_blocked",
                           "mx_blocked_grouped_bytes", "mx_scales_to_blocked_grouped"}
     for n in names:
@@ -73,6 +74,22 @@ def test_cast_dim1_3d_validation(lib):
     assert f(P_ODD, 2, 32, 32, P, P, None) == ERR_ALIGN
     assert f(P, 0, 32, 32, P, P, None) == OK
     assert f(None, 0, 32, 32, None, None, None) == OK
+
+
+def test_fused_blocked_validation(lib):
+    f = lib.mx_cast_dim0_dim1_blocked
+    assert f(None, 32, 32, P, P, P, P, None) == ERR_NULL
+    assert f(P, 33, 32, P, P, P, P, None) == ERR_SHAPE
+    assert f(P, 32, 32, P, None, None, None, None) == ERR_NULL
+    assert f(P, 32, 32, P, P_ODD, None, None, None) == ERR_ALIGN      # blocked scales need 16 B
+    assert f(P, 32, 32, None, None, P, ctypes.c_void_p(0x10008), None) == ERR_ALIGN
+    assert f(None, 0, 32, None, None, None, None, None) == OK
+    g = lib.mx_cast_dim1_3d_blocked
+    assert g(P, 2, 96, 32, P, P, None) == ERR_SHAPE                    # n not a multiple of 128
+    assert g(P, 2, 128, 40, P, P, None) == ERR_SHAPE
+    assert g(None, 2, 128, 32, P, P, None) == ERR_NULL
+    assert g(P, 2, 128, 32, P, P_ODD, None) == ERR_ALIGN
+    assert g(None, 0, 128, 32, None, None, None) == OK
 
 
 def test_blocked_sizes_match_oracle(lib, oracle_mod):
