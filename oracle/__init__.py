@@ -1,4 +1,5 @@
-"""CPU oracle for the bf16 -> MXFP8 cast and the 128x4 blocked scale layout.
+"""CPU oracle for the bf16 -> MXFP8 cast, the 128x4 blocked scale layout and
+the row-wise fp8 cast.
 
 TEST INFRASTRUCTURE ONLY.  The product library never imports, links or runs
 anything here; only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline
@@ -83,6 +84,16 @@ def _load():
         lib.mxo_to_blocked_grouped.argtypes = [_u8p, _i64, _i64, _i32p, ctypes.c_int32,
                                                ctypes.c_int32, _u8p, _i64, _i64p]
         lib.mxo_to_blocked_grouped.restype = ctypes.c_int
+        lib.mxo_bf16_round.argtypes = [ctypes.c_float]
+        lib.mxo_bf16_round.restype = ctypes.c_uint16
+        lib.mxo_e4m3fn_from_f32.argtypes = [ctypes.c_float]
+        lib.mxo_e4m3fn_from_f32.restype = ctypes.c_int
+        lib.mxo_rowwise_scale.argtypes = [ctypes.c_double]
+        lib.mxo_rowwise_scale.restype = ctypes.c_uint16
+        lib.mxo_rowwise_element.argtypes = [ctypes.c_double, ctypes.c_uint16]
+        lib.mxo_rowwise_element.restype = ctypes.c_int
+        lib.mxo_quantize_fp8_rowwise.argtypes = [_u16p, _i64, _i64, _u8p, _u16p]
+        lib.mxo_quantize_fp8_rowwise.restype = ctypes.c_int
         lib.mxo_num_threads.argtypes = []
         lib.mxo_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -179,6 +190,38 @@ def cast_dim1_3d(bits: np.ndarray):
     s = np.empty((e, k, n // 32), np.uint8)
     _check(_load().mxo_cast_dim1_3d(_ptr(w, _u16p), e, n, k, _ptr(q, _u8p), _ptr(s, _u8p)),
            "cast_dim1_3d")
+    return q, s
+
+
+# ---------------------------------------------------------------- row-wise fp8
+def bf16_round(f: float) -> int:
+    """float32 value -> bf16 bits, nearest-even (NaN -> 0x7FC0)."""
+    return int(_load().mxo_bf16_round(float(f)))
+
+
+def e4m3fn_from_f32(f: float) -> int:
+    """float32 value -> e4m3fn byte, nearest-even, no saturation (sign kept)."""
+    return int(_load().mxo_e4m3fn_from_f32(float(f)))
+
+
+def rowwise_scale(amax: float) -> int:
+    """bf16 bits of the row scale for a row amax (a bf16 value or NaN)."""
+    return int(_load().mxo_rowwise_scale(float(amax)))
+
+
+def rowwise_element(x: float, scale_bits: int) -> int:
+    """e4m3fn byte of the bf16 value x under a row scale given as bf16 bits."""
+    return int(_load().mxo_rowwise_element(float(x), int(scale_bits)))
+
+
+def quantize_fp8_rowwise(bits: np.ndarray):
+    """(R, C) bf16 bits -> q (R, C) e4m3fn bytes, scale (R,) bf16 bits."""
+    x = _bits(bits)
+    r, c = x.shape
+    q = np.empty((r, c), np.uint8)
+    s = np.zeros(r, np.uint16)
+    _check(_load().mxo_quantize_fp8_rowwise(_ptr(x, _u16p), r, c, _ptr(q, _u8p), _ptr(s, _u16p)),
+           "quantize_fp8_rowwise")
     return q, s
 
 

@@ -30,7 +30,9 @@
  *    int64 [G+1] offsets); Perf analysis item 4 (3D weights cast with the 2D
  *    dim1 kernel via a reshape).
  *  - "FP8 linear triton with row-wise scaling", quantize_fp8_rowwise: the e4m3
- *    maximum is finfo(float8_e4m3fn).max = 448.
+ *    maximum is finfo(float8_e4m3fn).max = 448; and the row-wise fp8 cast
+ *    itself (one bf16 scale per row), whose own readings are stated at
+ *    mxo_quantize_fp8_rowwise below.
  * The pages do not write out the MX scale rule, the rounding mode, the
  * treatment of Inf/NaN or the byte order inside a 128x4 tile.  The readings
  * taken here (each stated at the function that uses it) are:
@@ -56,6 +58,7 @@
 #define MXO_BLOCK 32          /* elements sharing one scale */
 #define MXO_E4M3_MAX 448.0    /* largest finite e4m3fn value */
 #define MXO_E4M3_EMAX 8       /* floor(log2(448)) */
+#define MXO_E4M3_NEXT 480.0   /* 1.875 * 2^8: the step past 448, which has no finite code */
 #define MXO_E8M0_NAN 0xFF
 
 enum { MXO_OK = 0, MXO_ERR_ARG = 1 };
@@ -381,6 +384,133 @@ int mxo_to_blocked_grouped(const uint8_t* s, int64_t rows, int64_t cols, const i
     }
     if (starts)
         starts[groups] = start;
+    return MXO_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* Row-wise fp8: one scale per row                                     */
+/* ------------------------------------------------------------------ */
+/*
+ * Source: the gist "FP8 linear triton with row-wise scaling",
+ * quantize_fp8_rowwise.  For a bf16 (rows, cols) matrix it takes, in order:
+ *   1. amax of |x| over each row, in bf16 (exact: a max of bf16 values);
+ *   2. scale = amax / 448, a bf16 tensor divided by a Python float: the
+ *      quotient is formed in float32 and rounded to bf16;
+ *   3. x converted to float32 and divided by the row's scale (float32);
+ *   4. that quotient converted to float8_e4m3fn.
+ * Readings, where the page leaves a step to the libraries it calls:
+ *   - float32 division is IEEE binary32, correctly rounded; float32 -> bf16
+ *     rounds to nearest, ties to even, and every NaN becomes 0x7FC0;
+ *   - float32 -> e4m3fn rounds to nearest, ties to even, without saturation:
+ *     a magnitude that rounds past 448 (the next step, 480, has no finite
+ *     code, so anything above 464) and +-Inf become NaN;
+ *   - a row holding a NaN has a NaN amax, so its scale is NaN and so is every
+ *     quotient; an all-zero row has scale 0 and its quotients 0/0 are NaN; a
+ *     row whose amax / 448 falls below the bf16 range gets scale 0 or a
+ *     subnormal scale and its larger elements overflow to NaN -- all as the
+ *     page's code computes them, with no guard added;
+ *   - the sign bit of every code, NaN codes included, is the sign bit of x
+ *     (the scale is never negative, so this is the quotient's sign wherever
+ *     the quotient is a number).
+ */
+
+/* binary32 quotient a / b, correctly rounded.  Formed in double and then
+ * rounded once to float: with 53 >= 2 * 24 + 2 bits the double rounding
+ * cannot differ from rounding the exact quotient (a classical result for
+ * the basic operations). */
+static float f32_quotient(float a, float b)
+{
+    return (float)((double)a / (double)b);
+}
+
+/* float32 value -> bf16 bit pattern, rounded to nearest, ties to even.
+ * Written as a comparison with the midpoint of the two bf16 neighbours (both
+ * exact in double), not as bit arithmetic. */
+uint16_t mxo_bf16_round(float f)
+{
+    if (isnan(f))
+        return 0x7FC0;
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    uint16_t sign = (uint16_t)((u >> 16) & 0x8000);
+    if (isinf(f))
+        return (uint16_t)(sign | 0x7F80);
+    double v = fabs((double)f);
+    uint16_t lo = (uint16_t)((u >> 16) & 0x7FFF);   /* largest bf16 magnitude <= |f| */
+    double v_lo = mxo_bf16_value(lo);
+    if (v_lo == v)
+        return (uint16_t)(sign | lo);
+    uint16_t hi = (uint16_t)(lo + 1);               /* 0x7F80 (Inf) stands for 2^128 */
+    double v_hi = hi == 0x7F80 ? ldexp(1.0, 128) : mxo_bf16_value(hi);
+    double mid = (v_lo + v_hi) / 2;
+    uint16_t pick = v < mid ? lo : v > mid ? hi : ((lo & 1) ? hi : lo);
+    return (uint16_t)(sign | pick);
+}
+
+/* float32 value -> e4m3fn byte without saturation (sign from the value). */
+int mxo_e4m3fn_from_f32(float f)
+{
+    int sign = signbit(f) ? 0x80 : 0x00;
+    if (isnan(f))
+        return 0x7F | sign;
+    double v = fabs((double)f);
+    if (v > (MXO_E4M3_MAX + MXO_E4M3_NEXT) / 2)   /* rounds to 480 or beyond: no finite code */
+        return 0x7F | sign;
+    init_codebook();
+    int best = 0;
+    double best_d = fabs(v - codebook[0]);
+    for (int c = 1; c < 127; ++c) {
+        double d = fabs(v - codebook[c]);
+        if (d < best_d || (d == best_d && (c & 1) == 0 && (best & 1) == 1)) {
+            best = c;
+            best_d = d;
+        }
+    }
+    return best | sign;
+}
+
+/* Scale of a row (bf16 bits) from its amax (a bf16 value, or NaN). */
+uint16_t mxo_rowwise_scale(double amax)
+{
+    if (isnan(amax))
+        return 0x7FC0;
+    return mxo_bf16_round(f32_quotient((float)amax, (float)MXO_E4M3_MAX));
+}
+
+/* Code of one element x (a bf16 value) under a row scale given as bf16 bits. */
+int mxo_rowwise_element(double x, uint16_t scale_bits)
+{
+    int sign = signbit(x) ? 0x80 : 0x00;
+    float q = f32_quotient((float)x, (float)mxo_bf16_value(scale_bits));
+    return (mxo_e4m3fn_from_f32(q) & 0x7F) | sign;
+}
+
+/* bf16 (rows, cols) -> q (rows, cols) e4m3fn bytes, scale (rows) bf16 bits. */
+int mxo_quantize_fp8_rowwise(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* q,
+                             uint16_t* scale)
+{
+    if (rows < 0 || cols < 0)
+        return MXO_ERR_ARG;
+    if (cols == 0)
+        return MXO_OK;
+    init_codebook();
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        const uint16_t* xr = x + r * cols;
+        double amax = 0.0;
+        int has_nan = 0;
+        for (int64_t i = 0; i < cols; ++i) {
+            double v = mxo_bf16_value(xr[i]);
+            if (isnan(v))
+                has_nan = 1;
+            else if (fabs(v) > amax)
+                amax = fabs(v);
+        }
+        uint16_t s = mxo_rowwise_scale(has_nan ? NAN : amax);
+        scale[r] = s;
+        for (int64_t i = 0; i < cols; ++i)
+            q[r * cols + i] = (uint8_t)mxo_rowwise_element(mxo_bf16_value(xr[i]), s);
+    }
     return MXO_OK;
 }
 
