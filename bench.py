@@ -13,15 +13,18 @@ sets written in the 128x4 blocked layout by the same launch.  Other workloads
              scales (4 groups along M, offsets on the device);
   kgroups    K-grouped layouts of (5120, 512), (8192, 4096), (2048, 4096)
              scale tensors (4 groups along K);
-  experts16  dim1 cast of (16, 8192, 5120) expert weights + per-expert
-             blocked layout of their scales;
+  experts16  dim1 cast of (16, 8192, 5120) expert weights with each
+             expert's scales written in the blocked layout by the same launch;
+  experts16_2launch  the same from the plain 3D cast + mx_scales_to_blocked;
+  rowwise16384  the row-wise fp8 cast (one bf16 scale per row) of the same
+             16384 x 16384 input;
   copy       a plain device-to-device copy of 1 GiB (counter calibration).
 
 Prints exactly one JSON line on stdout; progress goes to stderr.  The
 `roofline` object is for the dominant kernel (the cast): algorithmic bytes per
 launch divided by its average duration from HIP events recorded on the stream
-it runs on.  `cpu_baseline` times the CPU oracle on a bounded slice of the
-same input (rank 0, one GPU) and checks that slice against the GPU output.
+it runs on.  `cpu_baseline` times the CPU oracle on the same input (rank 0,
+one GPU) and checks every output byte against the GPU's.
 """
 from __future__ import annotations
 
@@ -150,27 +153,22 @@ def setup_square(dev, n=16384, fused=True):
         kern_name = "cast dim0+dim1"
 
     def cpu_baseline():
+        # the oracle on the whole input (a few seconds on the host's cores)
         import oracle
-        rows = 4096
-        sample = np.ascontiguousarray(bits[:rows])
         t0 = time.perf_counter()
-        r_q0, r_s0 = oracle.cast_dim0(sample)
-        r_q1, r_s1 = oracle.cast_dim1(sample)
+        r_q0, r_s0 = oracle.cast_dim0(bits)
+        r_q1, r_s1 = oracle.cast_dim1(bits)
         r_b0 = oracle.to_blocked(r_s0)
         r_b1 = oracle.to_blocked(r_s1)
         dt = time.perf_counter() - t0
-        nbytes = 4 * rows * n + r_b0.size + r_b1.size
-        # the sample's row scales are the first rows/128 row tiles of b0; its
-        # column scales are the first rows/128 column tiles of every row tile of b1
-        g_b1 = b1.view(pad(n, 128) // 128, pad(n // 32, 4) // 4, 512)[:, :rows // 128]
-        ok = (np.array_equal(q0[:rows].cpu().numpy(), r_q0)
-              and np.array_equal(q1[:, :rows].cpu().numpy(), r_q1)
-              and np.array_equal(b0[:rows].cpu().numpy().reshape(-1), r_b0)
-              and np.array_equal(g_b1.cpu().numpy().reshape(-1), r_b1))
+        nbytes = 4 * n * n + r_b0.size + r_b1.size
+        ok = (np.array_equal(q0.cpu().numpy(), r_q0) and np.array_equal(q1.cpu().numpy(), r_q1)
+              and np.array_equal(b0.cpu().numpy().reshape(-1), r_b0)
+              and np.array_equal(b1.cpu().numpy().reshape(-1), r_b1))
         return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
                 "kind": "oracle",
-                "sample": "rows 0..%d of the %dx%d input (dim0+dim1 cast, both scale sets in the "
-                          "blocked layout), %.1f s wall" % (rows, n, n, dt),
+                "sample": "the whole %dx%d input (dim0+dim1 cast, both scale sets in the blocked "
+                          "layout), %.1f s wall" % (n, n, dt),
                 "matches_gpu": bool(ok)}
 
     config = {"workload": "mx_cast_dim0_dim1%s %dx%d bf16 (heavy-tailed rows), both scale sets "
@@ -237,26 +235,73 @@ def setup_kgroups(dev):
     return step, nb, timer, big, "K-grouped layout (8192, 4096)", None, config
 
 
-def setup_experts(dev, experts=16, n=8192, k=5120):
+def setup_experts(dev, experts=16, n=8192, k=5120, fused=True):
     log("generating (%d, %d, %d) expert weights" % (experts, n, k))
     w = torch.empty((experts, n, k), dtype=torch.bfloat16, device=dev)
     for e in range(experts):
         w[e] = to_dev_bf16(workloads.expert_weight(e, n, k), dev)
     q = torch.empty((experts, k, n), dtype=torch.uint8, device=dev)
-    s = torch.empty((experts, k, n // 32), dtype=torch.uint8, device=dev)
     out = torch.empty((experts, pad(k, 128), pad(n // 32, 4)), dtype=torch.uint8, device=dev)
+    timer = Timer()
+    if fused:
+        def step():
+            with timer:
+                mx.mx_cast_dim1_3d_blocked(w, out=(q, out), raw=True)
+
+        cb = experts * n * k * 3 + out.numel()
+        nb = cb
+        name = "cast dim1 3D, blocked scales"
+    else:
+        s = torch.empty((experts, k, n // 32), dtype=torch.uint8, device=dev)
+
+        def step():
+            with timer:
+                mx.mx_cast_dim1_3d(w, out=(q, s), raw=True)
+            mx.mx_scales_to_blocked(s, out=out, raw=True)
+
+        cb = experts * n * k * 3 + experts * n * k // 32
+        nb = cb + blocked_bytes(k, n // 32, experts)
+        name = "cast dim1 3D"
+    config = {"workload": "%s (%d, %d, %d) bf16 + per-expert blocked scale layout%s"
+                          % ("mx_cast_dim1_3d_blocked" if fused else "mx_cast_dim1_3d", experts, n, k,
+                             "" if fused else " by mx_scales_to_blocked"),
+              "experts": experts, "n": n, "k": k}
+    return step, nb, timer, cb, name, None, config
+
+
+def setup_experts_2launch(dev):
+    return setup_experts(dev, fused=False)
+
+
+def setup_rowwise(dev, n=16384):
+    log("generating %dx%d heavy-tailed bf16 input" % (n, n))
+    bits = workloads.heavy_tailed_rows(n, n, seed=2)
+    x = to_dev_bf16(bits, dev)
+    q = torch.empty((n, n), dtype=torch.uint8, device=dev)
+    s = torch.empty(n, dtype=torch.int16, device=dev)
     timer = Timer()
 
     def step():
         with timer:
-            mx.mx_cast_dim1_3d(w, out=(q, s), raw=True)
-        mx.mx_scales_to_blocked(s, out=out, raw=True)
+            mx.mx_quantize_fp8_rowwise(x, out=(q, s), raw=True)
 
-    cb = experts * n * k * 3 + experts * n * k // 32
-    nb = cb + blocked_bytes(k, n // 32, experts)
-    config = {"workload": "mx_cast_dim1_3d (%d, %d, %d) bf16 + per-expert blocked layout"
-                          % (experts, n, k), "experts": experts, "n": n, "k": k}
-    return step, nb, timer, cb, "cast dim1 3D", None, config
+    nb = 3 * n * n + 2 * n   # read bf16, write e4m3fn, write one bf16 scale per row
+
+    def cpu_baseline():
+        # the oracle on the whole input (a few seconds on the host's cores)
+        import oracle
+        t0 = time.perf_counter()
+        r_q, r_s = oracle.quantize_fp8_rowwise(bits)
+        dt = time.perf_counter() - t0
+        ok = np.array_equal(q.cpu().numpy(), r_q) and np.array_equal(s.cpu().numpy().view(np.uint16), r_s)
+        return {"value": round(nb / dt / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
+                "kind": "oracle",
+                "sample": "the whole %dx%d input (row-wise fp8 cast), %.1f s wall" % (n, n, dt),
+                "matches_gpu": bool(ok)}
+
+    config = {"workload": "mx_quantize_fp8_rowwise %dx%d bf16 (heavy-tailed rows), one bf16 scale per row"
+                          % (n, n), "rows": n, "cols": n, "elem": "e4m3fn", "scale": "bf16 per row"}
+    return step, nb, timer, nb, "row-wise fp8 cast", cpu_baseline, config
 
 
 def setup_copy(dev, nbytes=1 << 30):
@@ -273,8 +318,8 @@ def setup_copy(dev, nbytes=1 << 30):
 
 
 WORKLOADS = {"square16384": setup_square, "square16384_3launch": setup_square_3launch,
-             "moe16640": setup_moe, "kgroups": setup_kgroups,
-             "experts16": setup_experts, "copy": setup_copy}
+             "moe16640": setup_moe, "kgroups": setup_kgroups, "rowwise16384": setup_rowwise,
+             "experts16": setup_experts, "experts16_2launch": setup_experts_2launch, "copy": setup_copy}
 
 
 def main():

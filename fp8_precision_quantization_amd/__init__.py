@@ -1,6 +1,6 @@
-"""libmxcast: bf16 -> MXFP8 casts and the 128x4 blocked e8m0 scale layout
-on AMD Instinct MI355X (gfx950), as hand-written HIP kernels behind a C ABI
-(include/mxcast.h).  This package is the thin Python binding over that ABI;
+"""libmxcast: bf16 -> MXFP8 casts, the 128x4 blocked e8m0 scale layout and
+the row-wise fp8 cast on AMD Instinct MI355X (gfx950), as hand-written HIP
+kernels behind a C ABI (include/mxcast.h).  This package is the thin Python binding over that ABI;
 the library is loaded on first use and its absence is an error."""
 from ._binding import (  # noqa: F401
     MX_BLOCK,
@@ -14,6 +14,7 @@ from ._binding import (  # noqa: F401
     mx_cast_dim0_dim1_blocked,
     mx_cast_dim1_3d,
     mx_cast_dim1_3d_blocked,
+    mx_quantize_fp8_rowwise,
     mx_scales_to_blocked,
     mx_scales_to_blocked_grouped,
     status_string,

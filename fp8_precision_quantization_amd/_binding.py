@@ -33,6 +33,7 @@ SIGNATURES = {
     "mx_cast_dim1_3d": ([_vp, _i64, _i64, _i64, _vp, _vp, _vp], ctypes.c_int),
     "mx_cast_dim0_dim1_blocked": ([_vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "mx_cast_dim1_3d_blocked": ([_vp, _i64, _i64, _i64, _vp, _vp, _vp], ctypes.c_int),
+    "mx_quantize_fp8_rowwise": ([_vp, _i64, _i64, _vp, _vp, _vp], ctypes.c_int),
     "mx_blocked_bytes": ([_i64, _i64, _i64], _i64),
     "mx_scales_to_blocked": ([_vp, _i64, _i64, _i64, _vp, _vp], ctypes.c_int),
     "mx_blocked_grouped_bytes": ([_i64, _i64, _i32, _i32], _i64),
@@ -179,6 +180,29 @@ def mx_cast_dim1_3d_blocked(w, out=None, raw: bool = False):
     _check(lib().mx_cast_dim1_3d_blocked(_ptr(w), e, n, k, _ptr(q), _ptr(s), _stream(w.device)),
            "mx_cast_dim1_3d_blocked")
     return _views(q, s, raw)
+
+
+def mx_quantize_fp8_rowwise(x, out=None, raw: bool = False):
+    """bf16 (R, C) -> (q (R, C) e4m3fn, scale (R,) bf16): one scale per row,
+    scale = amax / 448 (bf16), q = x / scale without saturation.  `out` may
+    hold preallocated (uint8 (R, C), bf16 or int16 (R,)) outputs.  raw=True
+    returns q as uint8 and the scale as its int16 bit patterns."""
+    _bf16_input(x, 2, "x")
+    rows, cols = x.shape
+    o = out if out is not None else (None, None)
+    q = _out(o[0], (rows, cols), x.device, "q")
+    if o[1] is None:
+        s = torch.empty(rows, dtype=torch.bfloat16, device=x.device)
+    else:
+        s = o[1]
+        if (s.dtype not in (torch.bfloat16, torch.int16) or tuple(s.shape) != (rows,)
+                or not s.is_contiguous() or s.device != x.device):
+            raise ValueError("scale must be a contiguous bf16 or int16 (%d,) tensor on %s" % (rows, x.device))
+    _check(lib().mx_quantize_fp8_rowwise(_ptr(x), rows, cols, _ptr(q), _ptr(s), _stream(x.device)),
+           "mx_quantize_fp8_rowwise")
+    if raw:
+        return q, s.view(torch.int16)
+    return q.view(torch.float8_e4m3fn), s.view(torch.bfloat16)
 
 
 def mx_blocked_bytes(batch: int, rows: int, cols: int) -> int:

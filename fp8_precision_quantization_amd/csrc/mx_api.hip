@@ -13,6 +13,7 @@ constexpr int64_t kMaxExtent = (int64_t)1 << 40;  // per-dimension bound, keeps 
 // with 32-bit row offsets: 32 * cols * 2 bytes must stay below 2^31.
 constexpr int64_t kMaxCastCols = (int64_t)1 << 25;
 constexpr int64_t kMaxGridBlocks = INT_MAX;
+constexpr int64_t kMaxRowwiseCols = (int64_t)1 << 30;
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
@@ -27,7 +28,7 @@ const char* mx_status_string(mx_status status) {
   switch (status) {
     case MX_OK: return "ok";
     case MX_ERR_NULL: return "a required pointer is NULL";
-    case MX_ERR_SHAPE: return "unsupported shape (negative, not a multiple of 32, or too large)";
+    case MX_ERR_SHAPE: return "unsupported shape (negative, not a multiple of the block, or too large)";
     case MX_ERR_GROUPS: return "num_groups or group_axis out of range";
     case MX_ERR_HIP: return "the HIP runtime rejected the launch";
     case MX_ERR_ALIGN: return "a pointer is not aligned as required";
@@ -178,6 +179,22 @@ mx_status mx_scales_to_blocked_grouped(const uint8_t* s, int64_t rows, int64_t c
     return MX_ERR_ALIGN;
   return from_hip(mx::launch_blocked_grouped(s, rows, cols, group_end_offsets, num_groups,
                                              group_axis, out, bytes, out_group_starts, stream));
+}
+
+mx_status mx_quantize_fp8_rowwise(const void* x, int64_t rows, int64_t cols, uint8_t* q,
+                                  uint16_t* scale, hipStream_t stream) {
+  if (rows < 0 || cols < 0 || rows > kMaxExtent || cols > kMaxRowwiseCols)
+    return MX_ERR_SHAPE;
+  if (rows == 0 || cols == 0)
+    return MX_OK;  // nothing to read or write; the pointers may be NULL
+  if (x == nullptr || q == nullptr || scale == nullptr)
+    return MX_ERR_NULL;
+  if (!aligned(x, 2) || !aligned(scale, 2))
+    return MX_ERR_ALIGN;
+  const bool vec = cols % 8 == 0 && aligned(x, 16) && aligned(q, 8);
+  if (mx::rowwise_grid_blocks(rows, cols, vec) > kMaxGridBlocks)
+    return MX_ERR_SHAPE;
+  return from_hip(mx::launch_rowwise(static_cast<const uint16_t*>(x), rows, cols, q, scale, vec, stream));
 }
 
 }  // extern "C"

@@ -22,4 +22,9 @@ hipError_t launch_blocked_grouped(const uint8_t* s, int64_t rows, int64_t cols, 
                                   int32_t groups, int32_t axis, uint8_t* out, int64_t out_bytes,
                                   int64_t* out_starts, hipStream_t stream);
 
+// Row-wise fp8 cast.  vec: cols % 8 == 0, x 16-byte and q 8-byte aligned.
+hipError_t launch_rowwise(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* q, uint16_t* s, bool vec,
+                          hipStream_t stream);
+int64_t rowwise_grid_blocks(int64_t rows, int64_t cols, bool vec);
+
 }  // namespace mx

@@ -16,6 +16,8 @@
  *  - "[mxfp8 moe training] parallelize along col blocks in scale blocked
  *    format kernel for groups along K", Changes: the blocked layout is built
  *    at a granularity of 128x4 scales.
+ *  - "FP8 linear triton with row-wise scaling", quantize_fp8_rowwise: the
+ *    row-wise fp8 cast (mx_quantize_fp8_rowwise, whose rule is stated there).
  *
  * MX rule (the pages do not spell it out; this is the reading implemented):
  *   amax  = max |x| over a block of 32 (NaN > +Inf > finite);
@@ -191,6 +193,29 @@ MX_API mx_status mx_scales_to_blocked_grouped(const uint8_t* s, int64_t rows, in
                                        const int32_t* group_end_offsets, int32_t num_groups,
                                        int32_t group_axis, uint8_t* out,
                                        int64_t* out_group_starts, hipStream_t stream);
+
+/*
+ * Row-wise fp8 cast with one bf16 scale per row (the gist "FP8 linear triton
+ * with row-wise scaling", quantize_fp8_rowwise).  For each row r of x:
+ *   scale[r] = amax_r / 448, the quotient of the row's bf16 amax |x| and the
+ *              largest e4m3fn value formed in binary32 and rounded to bf16
+ *              (nearest-even); a row holding a NaN has scale 0x7FC0;
+ *   q[r, c]  = binary32(x[r, c]) / scale[r] (correctly rounded) converted to
+ *              e4m3fn, nearest-even and NOT saturated: a magnitude above 464
+ *              (which would round to 480, past the largest code) and +-Inf
+ *              give NaN; the sign bit of every code is the sign bit of x.
+ * As in the page's code there is no guard: an all-zero row has scale 0 and
+ * NaN codes, and a row whose amax / 448 underflows bf16 gets a zero or
+ * subnormal scale under which its larger elements overflow to NaN.
+ *   x      bf16 (rows, cols) row-major contiguous; 2-byte aligned.
+ *   q      e4m3fn (rows, cols) row-major, rows * cols bytes.
+ *   scale  bf16 bit patterns, rows values; 2-byte aligned.
+ * rows, cols >= 0 and cols <= 2^30, else MX_ERR_SHAPE; rows or cols 0 writes
+ * nothing.  Any cols is accepted; the input is read once when cols % 8 == 0,
+ * cols <= 32768, x is 16-byte and q 8-byte aligned, and twice otherwise.
+ */
+MX_API mx_status mx_quantize_fp8_rowwise(const void* x, int64_t rows, int64_t cols, uint8_t* q,
+                                         uint16_t* scale, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -33,7 +33,7 @@ def declared_functions():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"mx_status_string", "mx_cast_dim0_dim1", "mx_cast_dim0_dim1_blocked",
-                          "mx_cast_dim1_3d", "mx_cast_dim1_3d_blocked",
+                          "mx_cast_dim1_3d", "mx_cast_dim1_3d_blocked", "mx_quantize_fp8_rowwise",
                           "mx_blocked_bytes", "mx_scales_to_blocked",
                           "mx_blocked_grouped_bytes", "mx_scales_to_blocked_grouped"}
     for n in names:
@@ -90,6 +90,19 @@ def test_fused_blocked_validation(lib):
     assert g(None, 2, 128, 32, P, P, None) == ERR_NULL
     assert g(P, 2, 128, 32, P, P_ODD, None) == ERR_ALIGN
     assert g(None, 0, 128, 32, None, None, None) == OK
+
+
+def test_rowwise_validation(lib):
+    f = lib.mx_quantize_fp8_rowwise
+    assert f(P, -1, 8, P, P, None) == ERR_SHAPE
+    assert f(P, 4, (1 << 30) + 1, P, P, None) == ERR_SHAPE
+    assert f(None, 4, 8, P, P, None) == ERR_NULL
+    assert f(P, 4, 8, None, P, None) == ERR_NULL
+    assert f(P, 4, 8, P, None, None) == ERR_NULL
+    assert f(ctypes.c_void_p(0x10001), 4, 8, P, P, None) == ERR_ALIGN
+    assert f(P, 4, 8, P, ctypes.c_void_p(0x10003), None) == ERR_ALIGN
+    assert f(None, 0, 8, None, None, None) == OK
+    assert f(None, 4, 0, None, None, None) == OK
 
 
 def test_blocked_sizes_match_oracle(lib, oracle_mod):
