@@ -1,5 +1,5 @@
 """CPU oracle for the bf16 -> MXFP8 cast, the 128x4 blocked scale layout and
-the row-wise fp8 cast.
+the row-wise and tensor-wise fp8 casts.
 
 TEST INFRASTRUCTURE ONLY.  The product library never imports, links or runs
 anything here; only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline
@@ -94,6 +94,8 @@ def _load():
         lib.mxo_rowwise_element.restype = ctypes.c_int
         lib.mxo_quantize_fp8_rowwise.argtypes = [_u16p, _i64, _i64, _u8p, _u16p]
         lib.mxo_quantize_fp8_rowwise.restype = ctypes.c_int
+        lib.mxo_quantize_fp8_tensorwise.argtypes = [_u16p, _i64, _u8p, _u16p]
+        lib.mxo_quantize_fp8_tensorwise.restype = ctypes.c_int
         lib.mxo_num_threads.argtypes = []
         lib.mxo_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -223,6 +225,16 @@ def quantize_fp8_rowwise(bits: np.ndarray):
     _check(_load().mxo_quantize_fp8_rowwise(_ptr(x, _u16p), r, c, _ptr(q, _u8p), _ptr(s, _u16p)),
            "quantize_fp8_rowwise")
     return q, s
+
+
+def quantize_fp8_tensorwise(bits: np.ndarray):
+    """bf16 bits of any shape -> (q same shape e4m3fn bytes, scale bf16 bits)."""
+    x = _bits(bits)
+    q = np.empty(x.shape, np.uint8)
+    s = np.zeros(1, np.uint16)
+    _check(_load().mxo_quantize_fp8_tensorwise(_ptr(x.reshape(-1), _u16p), x.size, _ptr(q.reshape(-1), _u8p),
+                                               _ptr(s, _u16p)), "quantize_fp8_tensorwise")
+    return q, int(s[0])
 
 
 # ---------------------------------------------------------------- layouts

@@ -33,6 +33,9 @@
  *    maximum is finfo(float8_e4m3fn).max = 448; and the row-wise fp8 cast
  *    itself (one bf16 scale per row), whose own readings are stated at
  *    mxo_quantize_fp8_rowwise below.
+ *  - "[float8nocompile]: Triton kernels for conversion to float8 dtypes for
+ *    forward pass of Float8LinearNoCompile": the tensor-wise fp8 cast (one
+ *    global amax), read at mxo_quantize_fp8_tensorwise below.
  * The pages do not write out the MX scale rule, the rounding mode, the
  * treatment of Inf/NaN or the byte order inside a 128x4 tile.  The readings
  * taken here (each stated at the function that uses it) are:
@@ -511,6 +514,46 @@ int mxo_quantize_fp8_rowwise(const uint16_t* x, int64_t rows, int64_t cols, uint
         for (int64_t i = 0; i < cols; ++i)
             q[r * cols + i] = (uint8_t)mxo_rowwise_element(mxo_bf16_value(xr[i]), s);
     }
+    return MXO_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* Tensor-wise fp8: one scale for the whole tensor                     */
+/* ------------------------------------------------------------------ */
+/*
+ * Source: "[float8nocompile]: Triton kernels for conversion to float8 dtypes
+ * for forward pass of Float8LinearNoCompile" (review thread): one amax for
+ * the whole tensor, found as per-block amaxes and then a global amax over
+ * them, before the elements are converted.  The page states the structure,
+ * not the formula.  Reading: the formula is the one the gist "FP8 linear
+ * triton with row-wise scaling" states for its fp8 cast, with the amax taken
+ * over every element instead of over a row -- bf16 amax; scale = amax / 448
+ * through float32 to bf16; float32 x / scale to e4m3fn without saturation;
+ * the same NaN and sign readings as the row-wise cast above.  The amax is a
+ * max, so the order of the blocks cannot change it; the oracle takes it in
+ * one plain loop.
+ */
+int mxo_quantize_fp8_tensorwise(const uint16_t* x, int64_t n, uint8_t* q, uint16_t* scale)
+{
+    if (n < 0)
+        return MXO_ERR_ARG;
+    if (n == 0)
+        return MXO_OK;
+    init_codebook();
+    double amax = 0.0;
+    int has_nan = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        double v = mxo_bf16_value(x[i]);
+        if (isnan(v))
+            has_nan = 1;
+        else if (fabs(v) > amax)
+            amax = fabs(v);
+    }
+    uint16_t s = mxo_rowwise_scale(has_nan ? NAN : amax);
+    *scale = s;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i)
+        q[i] = (uint8_t)mxo_rowwise_element(mxo_bf16_value(x[i]), s);
     return MXO_OK;
 }
 
