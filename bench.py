@@ -18,6 +18,8 @@ sets written in the 128x4 blocked layout by the same launch.  Other workloads
   experts16_2launch  the same from the plain 3D cast + mx_scales_to_blocked;
   rowwise16384  the row-wise fp8 cast (one bf16 scale per row) of the same
              16384 x 16384 input;
+  tensorwise16384  the tensor-wise fp8 cast (one bf16 scale, two-stage amax)
+             of the same input;
   copy       a plain device-to-device copy of 1 GiB (counter calibration).
 
 Prints exactly one JSON line on stdout; progress goes to stderr.  The
@@ -304,6 +306,40 @@ def setup_rowwise(dev, n=16384):
     return step, nb, timer, nb, "row-wise fp8 cast", cpu_baseline, config
 
 
+def setup_tensorwise(dev, n=16384):
+    log("generating %dx%d heavy-tailed bf16 input" % (n, n))
+    bits = workloads.heavy_tailed_rows(n, n, seed=2)
+    x = to_dev_bf16(bits, dev)
+    q = torch.empty((n, n), dtype=torch.uint8, device=dev)
+    s = torch.empty(1, dtype=torch.int16, device=dev)
+    ws = torch.empty(mx.mx_tensorwise_workspace_bytes(n * n), dtype=torch.uint8, device=dev)
+    timer = Timer()
+
+    def step():
+        with timer:
+            mx.mx_quantize_fp8_tensorwise(x, out=(q, s), workspace=ws, raw=True)
+
+    # the amax pass must end before any element is converted and the input
+    # does not fit on chip: it is read twice (2 + 2 B), codes written (1 B)
+    nb = 5 * n * n + 2
+
+    def cpu_baseline():
+        import oracle
+        t0 = time.perf_counter()
+        r_q, r_s = oracle.quantize_fp8_tensorwise(bits)
+        dt = time.perf_counter() - t0
+        ok = np.array_equal(q.cpu().numpy(), r_q) and int(s.cpu().numpy().view(np.uint16)[0]) == r_s
+        return {"value": round(nb / dt / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
+                "kind": "oracle",
+                "sample": "the whole %dx%d input (tensor-wise fp8 cast), %.1f s wall" % (n, n, dt),
+                "matches_gpu": bool(ok)}
+
+    config = {"workload": "mx_quantize_fp8_tensorwise %dx%d bf16 (heavy-tailed rows), one bf16 scale, "
+                          "two-stage amax" % (n, n), "rows": n, "cols": n, "elem": "e4m3fn",
+              "scale": "bf16 per tensor"}
+    return step, nb, timer, nb, "tensor-wise fp8 cast (amax + cast launches)", cpu_baseline, config
+
+
 def setup_copy(dev, nbytes=1 << 30):
     a = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
     b = torch.empty_like(a)
@@ -319,6 +355,7 @@ def setup_copy(dev, nbytes=1 << 30):
 
 WORKLOADS = {"square16384": setup_square, "square16384_3launch": setup_square_3launch,
              "moe16640": setup_moe, "kgroups": setup_kgroups, "rowwise16384": setup_rowwise,
+             "tensorwise16384": setup_tensorwise,
              "experts16": setup_experts, "experts16_2launch": setup_experts_2launch, "copy": setup_copy}
 
 

@@ -16,7 +16,7 @@ import torch
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmxcast.so")
 
-MX_OK, MX_ERR_NULL, MX_ERR_SHAPE, MX_ERR_GROUPS, MX_ERR_HIP, MX_ERR_ALIGN = range(6)
+MX_OK, MX_ERR_NULL, MX_ERR_SHAPE, MX_ERR_GROUPS, MX_ERR_HIP, MX_ERR_ALIGN, MX_ERR_WORKSPACE = range(7)
 MX_BLOCK = 32
 MX_MAX_GROUPS = 1024
 
@@ -34,6 +34,8 @@ SIGNATURES = {
     "mx_cast_dim0_dim1_blocked": ([_vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "mx_cast_dim1_3d_blocked": ([_vp, _i64, _i64, _i64, _vp, _vp, _vp], ctypes.c_int),
     "mx_quantize_fp8_rowwise": ([_vp, _i64, _i64, _vp, _vp, _vp], ctypes.c_int),
+    "mx_tensorwise_workspace_bytes": ([_i64], _i64),
+    "mx_quantize_fp8_tensorwise": ([_vp, _i64, _vp, _vp, _vp, _i64, _vp], ctypes.c_int),
     "mx_blocked_bytes": ([_i64, _i64, _i64], _i64),
     "mx_scales_to_blocked": ([_vp, _i64, _i64, _i64, _vp, _vp], ctypes.c_int),
     "mx_blocked_grouped_bytes": ([_i64, _i64, _i32, _i32], _i64),
@@ -200,6 +202,43 @@ def mx_quantize_fp8_rowwise(x, out=None, raw: bool = False):
             raise ValueError("scale must be a contiguous bf16 or int16 (%d,) tensor on %s" % (rows, x.device))
     _check(lib().mx_quantize_fp8_rowwise(_ptr(x), rows, cols, _ptr(q), _ptr(s), _stream(x.device)),
            "mx_quantize_fp8_rowwise")
+    if raw:
+        return q, s.view(torch.int16)
+    return q.view(torch.float8_e4m3fn), s.view(torch.bfloat16)
+
+
+def mx_tensorwise_workspace_bytes(n: int) -> int:
+    return lib().mx_tensorwise_workspace_bytes(n)
+
+
+def mx_quantize_fp8_tensorwise(x, out=None, workspace=None, raw: bool = False):
+    """bf16 tensor of any shape -> (q same shape e4m3fn, scale bf16 (1,)): one
+    scale for the whole tensor, scale = amax / 448 (bf16), q = x / scale
+    without saturation.  `out` may hold preallocated (uint8 q, bf16 or int16
+    (1,) scale); `workspace` a uint8 device tensor of at least
+    mx_tensorwise_workspace_bytes(numel) bytes (allocated here if None)."""
+    if not isinstance(x, torch.Tensor) or not x.is_cuda or x.dtype != torch.bfloat16:
+        raise ValueError("x must be a bfloat16 CUDA (HIP) tensor")
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    n = x.numel()
+    o = out if out is not None else (None, None)
+    q = _out(o[0], tuple(x.shape), x.device, "q")
+    if o[1] is None:
+        s = torch.empty(1, dtype=torch.bfloat16, device=x.device)
+    else:
+        s = o[1]
+        if (s.dtype not in (torch.bfloat16, torch.int16) or s.numel() != 1 or not s.is_contiguous()
+                or s.device != x.device):
+            raise ValueError("scale must be a one-element bf16 or int16 tensor on %s" % x.device)
+    need = max(lib().mx_tensorwise_workspace_bytes(n), 0)
+    if workspace is None:
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=x.device)
+    elif not (workspace.is_cuda and workspace.is_contiguous() and workspace.device == x.device):
+        raise ValueError("workspace must be a contiguous tensor on %s" % x.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().mx_quantize_fp8_tensorwise(_ptr(x), n, _ptr(q), _ptr(s), _ptr(workspace), ws_bytes,
+                                            _stream(x.device)), "mx_quantize_fp8_tensorwise")
     if raw:
         return q, s.view(torch.int16)
     return q.view(torch.float8_e4m3fn), s.view(torch.bfloat16)

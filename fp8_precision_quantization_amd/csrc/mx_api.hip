@@ -32,6 +32,7 @@ const char* mx_status_string(mx_status status) {
     case MX_ERR_GROUPS: return "num_groups or group_axis out of range";
     case MX_ERR_HIP: return "the HIP runtime rejected the launch";
     case MX_ERR_ALIGN: return "a pointer is not aligned as required";
+    case MX_ERR_WORKSPACE: return "the workspace is smaller than required";
   }
   return "unknown status";
 }
@@ -195,6 +196,31 @@ mx_status mx_quantize_fp8_rowwise(const void* x, int64_t rows, int64_t cols, uin
   if (mx::rowwise_grid_blocks(rows, cols, vec) > kMaxGridBlocks)
     return MX_ERR_SHAPE;
   return from_hip(mx::launch_rowwise(static_cast<const uint16_t*>(x), rows, cols, q, scale, vec, stream));
+}
+
+int64_t mx_tensorwise_workspace_bytes(int64_t n) {
+  if (n < 0 || n > kMaxExtent)
+    return -1;
+  return 4 * mx::tensorwise_partials(n);
+}
+
+mx_status mx_quantize_fp8_tensorwise(const void* x, int64_t n, uint8_t* q, uint16_t* scale, void* workspace,
+                                     int64_t workspace_bytes, hipStream_t stream) {
+  if (n < 0 || n > kMaxExtent)
+    return MX_ERR_SHAPE;
+  if (n == 0)
+    return MX_OK;  // nothing to read or write; the pointers may be NULL
+  if (x == nullptr || q == nullptr || scale == nullptr || workspace == nullptr)
+    return MX_ERR_NULL;
+  if (workspace_bytes < mx_tensorwise_workspace_bytes(n))
+    return MX_ERR_WORKSPACE;
+  if (!aligned(x, 2) || !aligned(scale, 2) || !aligned(workspace, 4))
+    return MX_ERR_ALIGN;
+  const bool vec = aligned(x, 16) && aligned(q, 8);
+  if (mx::tensorwise_cast_blocks(n, vec) > kMaxGridBlocks)
+    return MX_ERR_SHAPE;
+  return from_hip(mx::launch_tensorwise(static_cast<const uint16_t*>(x), n, q, scale,
+                                        static_cast<uint32_t*>(workspace), vec, stream));
 }
 
 }  // extern "C"

@@ -27,4 +27,11 @@ hipError_t launch_rowwise(const uint16_t* x, int64_t rows, int64_t cols, uint8_t
                           hipStream_t stream);
 int64_t rowwise_grid_blocks(int64_t rows, int64_t cols, bool vec);
 
+// Tensor-wise fp8 cast (two launches); partial holds tensorwise_partials(n)
+// words.  vec: x 16-byte and q 8-byte aligned.
+hipError_t launch_tensorwise(const uint16_t* x, int64_t n, uint8_t* q, uint16_t* scale, uint32_t* partial,
+                             bool vec, hipStream_t stream);
+int64_t tensorwise_partials(int64_t n);
+int64_t tensorwise_cast_blocks(int64_t n, bool vec);
+
 }  // namespace mx

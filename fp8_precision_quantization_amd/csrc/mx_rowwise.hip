@@ -18,128 +18,16 @@
 // of 16-byte chunks, go to a two-pass kernel that streams the row twice
 // (the second pass mostly hits the cache).
 //
-// The quotient.  For a normal, finite scale s the kernel forms r = 1/s once
-// per row (correctly rounded), then per element q0 = x * r, the exact
-// residual e = x - q0 * s by one fma, and q = q0 + e * r by another.  With r
-// correctly rounded and q0 within an ulp of x / s this is the correctly
-// rounded binary32 quotient (Markstein's theorem), three operations instead
-// of a full IEEE division sequence.  For such a scale |x / s| <= 448 * (1 +
-// 2^-8) < 464, so no code overflows.  Rows whose scale is zero, subnormal,
-// Inf or NaN (uniform per row) take a general path with IEEE division and an
-// explicit overflow test.  The e4m3 rounding is gfx950's scaled convert with
-// scale 1, fed magnitudes below 448.
-#include "mx_device.h"
+// The scale and the element quotient are mx_fp8.h's; rows whose scale is
+// zero, subnormal, Inf or NaN are uniform per row and take its general path.
+#include "mx_fp8.h"
 #include "mxcast.h"
 #include "mx_launch.h"
 
 namespace mx {
 
 constexpr int kRowThreads = 256;
-constexpr float kE4m3Max = 448.0f;
-constexpr float kE4m3Overflow = 464.0f;   // midpoint of 448 and 480 (no finite code)
 constexpr int kLoadNTRow = 2;             // cache-policy bits of the input loads: nt
-
-struct RowScale {
-  uint32_t bits;  // bf16 bits of the scale
-  float s;        // the scale as binary32 (exact)
-  float r;        // 1 / s, correctly rounded (fast path)
-  bool fast;      // s normal and finite
-};
-
-// Row scale from the row's amax magnitude bits (NaN > Inf > finite).
-__device__ __forceinline__ RowScale row_scale(uint32_t amax) {
-  RowScale p;
-  if (amax > kInfBits) {
-    p.bits = 0x7FC0u;
-  } else if (amax == kInfBits) {
-    p.bits = kInfBits;
-  } else {
-    // binary32 quotient (IEEE division), then nearest-even to the top 16
-    // bits: adding 0x7FFF plus the kept LSB carries exactly when the dropped
-    // half is above one half, or equal to it with an odd LSB.
-    const uint32_t u = __float_as_uint(__uint_as_float(amax << 16) / kE4m3Max);
-    p.bits = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-  }
-  p.s = __uint_as_float(p.bits << 16);
-  const uint32_t ef = p.bits & kInfBits;
-  p.fast = ef != 0 && ef != kInfBits;
-  p.r = 1.0f / p.s;
-  return p;
-}
-
-// Correctly rounded |x| / s for a normal finite s with r = RN(1 / s).
-__device__ __forceinline__ float div_fast(float x, float s, float r) {
-  const float q0 = x * r;
-  const float e = __builtin_fmaf(-q0, s, x);
-  return __builtin_fmaf(e, r, q0);
-}
-
-// Magnitude code of a quotient when the scale is not normal and finite: NaN
-// and anything past 464 (Inf included) has no finite code; (448, 464] rounds
-// to 448.
-__device__ __forceinline__ float slow_clamp(float q, bool& nan) {
-  nan = !(q <= kE4m3Overflow);
-  return __builtin_fminf(q, kE4m3Max);
-}
-
-// Sign bits of four bf16 values (two packed pairs) in the code byte positions.
-__device__ __forceinline__ uint32_t signs4(uint32_t x01, uint32_t x23) {
-  return __builtin_amdgcn_perm(x23, x01, 0x07050301u) & 0x80808080u;
-}
-
-// Eight bf16 values (one 16-byte chunk) -> eight e4m3fn bytes.
-template <bool FAST>
-__device__ __forceinline__ uint2 quant8(const uint4& d, const RowScale& p) {
-  const uint32_t w[4] = {d.x, d.y, d.z, d.w};
-  uint32_t out[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    float m[4];
-    bool nan[4] = {false, false, false, false};
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const uint32_t v = w[2 * h + k] & kMagMask2;
-      const float lo = __uint_as_float(v << 16);
-      const float hi = __uint_as_float(v & 0xFFFF0000u);
-      if (FAST) {
-        m[2 * k] = div_fast(lo, p.s, p.r);
-        m[2 * k + 1] = div_fast(hi, p.s, p.r);
-      } else {
-        m[2 * k] = slow_clamp(lo / p.s, nan[2 * k]);
-        m[2 * k + 1] = slow_clamp(hi / p.s, nan[2 * k + 1]);
-      }
-    }
-    i16x2 r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32((i16x2){0, 0}, m[0], m[1], 1.0f, false);
-    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, m[2], m[3], 1.0f, true);
-    uint32_t c = as_u32(r);
-    if (!FAST) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        if (nan[k])
-          c |= 0x7Fu << (8 * k);
-    }
-    out[h] = c | signs4(w[2 * h], w[2 * h + 1]);
-  }
-  return make_uint2(out[0], out[1]);
-}
-
-// One bf16 value -> its e4m3fn byte (the streaming kernel's ragged path).
-__device__ __forceinline__ uint32_t quant1(uint32_t x, const RowScale& p) {
-  const uint4 d = make_uint4(x & 0xFFFFu, 0, 0, 0);
-  return (p.fast ? quant8<true>(d, p) : quant8<false>(d, p)).x & 0xFFu;
-}
-
-__device__ __forceinline__ uint32_t chunk_amax(const uint4& d) {
-  return max2(max2(mag2(d.x), mag2(d.y)), max2(mag2(d.z), mag2(d.w)));
-}
-
-// Max over the 64 lanes of a wave (every lane gets it).
-__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1)
-    v = max(v, (uint32_t)__shfl_xor((int)v, o));
-  return v;
-}
 
 template <int WPR, int K>
 __global__ __launch_bounds__(kRowThreads) void rowwise_kernel(const uint16_t* __restrict__ x, int64_t rows,
@@ -179,7 +67,7 @@ __global__ __launch_bounds__(kRowThreads) void rowwise_kernel(const uint16_t* __
     for (int i = 0; i < WPR; ++i)
       m = max(m, wave_amax[first + i]);
   }
-  const RowScale p = row_scale(m);
+  const Fp8Scale p = fp8_scale(m);
   if (row_on && wr == 0 && lane == 0)
     scale[row] = (uint16_t)p.bits;
   if (p.fast) {
@@ -225,7 +113,7 @@ __global__ __launch_bounds__(kRowThreads) void rowwise_stream_kernel(const uint1
     wave_amax[wave] = m;
   lds_barrier();
   m = max(max(wave_amax[0], wave_amax[1]), max(wave_amax[2], wave_amax[3]));
-  const RowScale p = row_scale(m);
+  const Fp8Scale p = fp8_scale(m);
   if (t == 0)
     scale[row] = (uint16_t)p.bits;
   if (VEC) {
@@ -260,7 +148,7 @@ static RowShape row_shape(int64_t cols) {
     return {1, k};
   }
   if (cols <= kRegCols) {
-    int k = 2;
+    int k = 4;   // more than 512 chunks: at least 4 per lane of the workgroup
     while (4 * 64 * k < chunks)
       k *= 2;
     return {4, k};
@@ -298,7 +186,6 @@ hipError_t launch_rowwise(const uint16_t* x, int64_t rows, int64_t cols, uint8_t
   }
   if (sh.wpr == 4) {
     switch (sh.k) {
-      case 2: return launch_rows<4, 2>(x, rows, cols, q, s, stream);
       case 4: return launch_rows<4, 4>(x, rows, cols, q, s, stream);
       case 8: return launch_rows<4, 8>(x, rows, cols, q, s, stream);
       default: return launch_rows<4, 16>(x, rows, cols, q, s, stream);

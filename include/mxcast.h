@@ -18,6 +18,9 @@
  *    at a granularity of 128x4 scales.
  *  - "FP8 linear triton with row-wise scaling", quantize_fp8_rowwise: the
  *    row-wise fp8 cast (mx_quantize_fp8_rowwise, whose rule is stated there).
+ *  - "[float8nocompile]: Triton kernels for conversion to float8 dtypes for
+ *    forward pass of Float8LinearNoCompile": the tensor-wise fp8 cast with a
+ *    two-stage global amax (mx_quantize_fp8_tensorwise).
  *
  * MX rule (the pages do not spell it out; this is the reading implemented):
  *   amax  = max |x| over a block of 32 (NaN > +Inf > finite);
@@ -35,8 +38,8 @@
  *
  * Conventions for every call below:
  *  - All array arguments are DEVICE pointers, contiguous, row-major.
- *  - The caller owns every buffer and the stream.  The library allocates
- *    nothing, keeps no state, never synchronises and never reads device
+ *  - The caller owns every buffer (scratch included) and the stream.  The
+ *    library allocates nothing, keeps no state, never synchronises and never reads device
  *    memory from the host; all work is enqueued on `stream` (0 = the null
  *    stream) and runs asynchronously.
  *  - Arguments are validated on the host before any HIP call; a rejected
@@ -68,7 +71,8 @@ typedef enum {
                         /* is required, or beyond the supported maximum        */
     MX_ERR_GROUPS = 3,  /* num_groups outside [1, MX_MAX_GROUPS] or bad axis   */
     MX_ERR_HIP = 4,     /* the HIP runtime rejected a launch                   */
-    MX_ERR_ALIGN = 5    /* a pointer lacks the alignment stated for it         */
+    MX_ERR_ALIGN = 5,   /* a pointer lacks the alignment stated for it         */
+    MX_ERR_WORKSPACE = 6 /* a caller-provided workspace is too small           */
 } mx_status;
 
 #define MX_BLOCK 32          /* elements per scale block                  */
@@ -216,6 +220,32 @@ MX_API mx_status mx_scales_to_blocked_grouped(const uint8_t* s, int64_t rows, in
  */
 MX_API mx_status mx_quantize_fp8_rowwise(const void* x, int64_t rows, int64_t cols, uint8_t* q,
                                          uint16_t* scale, hipStream_t stream);
+
+/*
+ * Tensor-wise fp8 cast: one bf16 scale for the whole tensor, from a global
+ * amax found in two stages ("[float8nocompile]: Triton kernels for
+ * conversion to float8 dtypes for forward pass of Float8LinearNoCompile",
+ * review thread: block amaxes computed in parallel into a buffer, a global
+ * amax from them, then the conversion).  With amax = max |x| over all n
+ * elements, scale and codes follow mx_quantize_fp8_rowwise's rule:
+ *   *scale = amax / 448 through binary32 to bf16 (0x7FC0 if any x is NaN);
+ *   q[i]   = e4m3fn(binary32(x[i]) / *scale), not saturated, sign of x.
+ *   x          bf16, n elements of any shape, contiguous; 2-byte aligned.
+ *   q          n bytes.
+ *   scale      one bf16 (2 bytes, 2-byte aligned), written by the call.
+ *   workspace  device scratch of at least mx_tensorwise_workspace_bytes(n)
+ *              bytes, 4-byte aligned, owned by the caller; it holds the
+ *              block amaxes between the two launches, needs no clearing and
+ *              must not be used by another call until this one has run.
+ * n < 0 or n > 2^40 -> MX_ERR_SHAPE; n == 0 writes nothing; a workspace
+ * smaller than required -> MX_ERR_WORKSPACE.  Two kernels are enqueued; the
+ * input is read twice (the second time partly from the memory-side cache).
+ * Fastest with x 16-byte and q 8-byte aligned.
+ */
+MX_API int64_t mx_tensorwise_workspace_bytes(int64_t n);
+MX_API mx_status mx_quantize_fp8_tensorwise(const void* x, int64_t n, uint8_t* q, uint16_t* scale,
+                                            void* workspace, int64_t workspace_bytes,
+                                            hipStream_t stream);
 
 #ifdef __cplusplus
 }

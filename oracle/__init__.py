@@ -92,6 +92,8 @@ def _load():
         lib.mxo_rowwise_scale.restype = ctypes.c_uint16
         lib.mxo_rowwise_element.argtypes = [ctypes.c_double, ctypes.c_uint16]
         lib.mxo_rowwise_element.restype = ctypes.c_int
+        lib.mxo_rowwise_elements.argtypes = [_u16p, _i64, ctypes.c_uint16, _u8p]
+        lib.mxo_rowwise_elements.restype = None
         lib.mxo_quantize_fp8_rowwise.argtypes = [_u16p, _i64, _i64, _u8p, _u16p]
         lib.mxo_quantize_fp8_rowwise.restype = ctypes.c_int
         lib.mxo_quantize_fp8_tensorwise.argtypes = [_u16p, _i64, _u8p, _u16p]
@@ -214,6 +216,14 @@ def rowwise_scale(amax: float) -> int:
 def rowwise_element(x: float, scale_bits: int) -> int:
     """e4m3fn byte of the bf16 value x under a row scale given as bf16 bits."""
     return int(_load().mxo_rowwise_element(float(x), int(scale_bits)))
+
+
+def rowwise_elements(bits: np.ndarray, scale_bits: int) -> np.ndarray:
+    """e4m3fn bytes of bf16 values under one scale given as bf16 bits."""
+    x = _bits(bits).reshape(-1)
+    q = np.empty(x.shape, np.uint8)
+    _load().mxo_rowwise_elements(_ptr(x, _u16p), x.size, int(scale_bits), _ptr(q, _u8p))
+    return q.reshape(bits.shape)
 
 
 def quantize_fp8_rowwise(bits: np.ndarray):

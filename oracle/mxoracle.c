@@ -488,6 +488,15 @@ int mxo_rowwise_element(double x, uint16_t scale_bits)
     return (mxo_e4m3fn_from_f32(q) & 0x7F) | sign;
 }
 
+/* The element rule over n bf16 values under one scale given as bf16 bits. */
+void mxo_rowwise_elements(const uint16_t* x, int64_t n, uint16_t scale_bits, uint8_t* q)
+{
+    init_codebook();
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i)
+        q[i] = (uint8_t)mxo_rowwise_element(mxo_bf16_value(x[i]), scale_bits);
+}
+
 /* bf16 (rows, cols) -> q (rows, cols) e4m3fn bytes, scale (rows) bf16 bits. */
 int mxo_quantize_fp8_rowwise(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* q,
                              uint16_t* scale)

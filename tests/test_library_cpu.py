@@ -11,7 +11,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mxcast.h")
 
-OK, ERR_NULL, ERR_SHAPE, ERR_GROUPS, ERR_HIP, ERR_ALIGN = range(6)
+OK, ERR_NULL, ERR_SHAPE, ERR_GROUPS, ERR_HIP, ERR_ALIGN, ERR_WORKSPACE = range(7)
 P = ctypes.c_void_p(0x10000)       # well aligned, never dereferenced
 P_ODD = ctypes.c_void_p(0x10001)   # misaligned
 
@@ -34,6 +34,7 @@ def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"mx_status_string", "mx_cast_dim0_dim1", "mx_cast_dim0_dim1_blocked",
                           "mx_cast_dim1_3d", "mx_cast_dim1_3d_blocked", "mx_quantize_fp8_rowwise",
+                          "mx_tensorwise_workspace_bytes", "mx_quantize_fp8_tensorwise",
                           "mx_blocked_bytes", "mx_scales_to_blocked",
                           "mx_blocked_grouped_bytes", "mx_scales_to_blocked_grouped"}
     for n in names:
@@ -103,6 +104,24 @@ def test_rowwise_validation(lib):
     assert f(P, 4, 8, P, ctypes.c_void_p(0x10003), None) == ERR_ALIGN
     assert f(None, 0, 8, None, None, None) == OK
     assert f(None, 4, 0, None, None, None) == OK
+
+
+def test_tensorwise_validation(lib):
+    ws = lib.mx_tensorwise_workspace_bytes
+    assert ws(-1) == -1 and ws((1 << 40) + 1) == -1
+    assert ws(0) == 4 and ws(1) == 4 and ws(32768) == 4 and ws(32769) == 8
+    assert ws(1 << 40) == 4 * 2048                  # at most 2048 block amaxes
+    f = lib.mx_quantize_fp8_tensorwise
+    assert f(P, -1, P, P, P, 1 << 20, None) == ERR_SHAPE
+    assert f(None, 0, None, None, None, 0, None) == OK
+    assert f(None, 64, P, P, P, 64, None) == ERR_NULL
+    assert f(P, 64, P, P, None, 64, None) == ERR_NULL
+    assert f(P, 64, P, P, P, 3, None) == ERR_WORKSPACE
+    assert f(P, 1 << 20, P, P, P, 4 * 31, None) == ERR_WORKSPACE
+    assert f(P_ODD, 64, P, P, P, 64, None) == ERR_ALIGN
+    assert f(P, 64, P, P_ODD, P, 64, None) == ERR_ALIGN
+    assert f(P, 64, P, P, ctypes.c_void_p(0x10002), 64, None) == ERR_ALIGN
+    assert lib.mx_status_string(ERR_WORKSPACE) == b"the workspace is smaller than required"
 
 
 def test_blocked_sizes_match_oracle(lib, oracle_mod):
