@@ -22,6 +22,10 @@ sets written in the 128x4 blocked layout by the same launch.  Other workloads
              of the same input;
   copy       a plain device-to-device copy of 1 GiB (counter calibration).
 
+Each workload's calls are validated once through the Python binding; the
+timed loop then calls the same C-ABI entry points with their arguments
+marshalled in advance, so the host keeps ahead of the GPU.
+
 Prints exactly one JSON line on stdout; progress goes to stderr.  The
 `roofline` object is for the dominant kernel (the cast): algorithmic bytes per
 launch divided by its average duration from HIP events recorded on the stream
@@ -31,6 +35,7 @@ one GPU) and checks every output byte against the GPU's.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -99,24 +104,76 @@ def counter_traffic():
 
 
 class Timer:
-    """HIP events bracketing one kernel on torch's current stream (the stream
-    the library launches on)."""
+    """Kernel time from HIP events on torch's current stream (the stream the
+    library launches on).
 
-    def __init__(self):
-        self.pairs = []
+    whole_step=True: the step is the timed operation alone, so one event pair
+    around the whole timed region gives its average duration (region / steps)
+    and the launches run back to back.  Otherwise a pair of events brackets
+    each timed launch inside the step (a timed event record between two
+    kernels costs a few microseconds, so this is kept to steps with several
+    launches, where one of them must be isolated).  Events are created before
+    the timed steps so that the loop stays cheap on the host."""
+
+    def __init__(self, whole_step=False):
+        self.whole_step = whole_step
+        self.events = []
+        self.used = 0
+        self.region = None
+
+    def reserve(self, n):
+        if self.whole_step:
+            return
+        while len(self.events) < n:
+            self.events.append((torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
+        self.used = 0
 
     def __enter__(self):
-        self.a = torch.cuda.Event(enable_timing=True)
-        self.b = torch.cuda.Event(enable_timing=True)
-        self.a.record()
+        if self.whole_step:
+            return self
+        if self.used == len(self.events):
+            self.reserve(self.used + 64)
+            self.used = len(self.events) - 64
+        self.events[self.used][0].record()
         return self
 
     def __exit__(self, *exc):
-        self.b.record()
-        self.pairs.append((self.a, self.b))
+        if self.whole_step:
+            return
+        self.events[self.used][1].record()
+        self.used += 1
+
+    def clear(self):
+        self.used = 0
+
+    def start_region(self):
+        self.region = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        self.region[0].record()
+
+    def end_region(self, steps):
+        self.region[1].record()
+        self.steps = steps
 
     def mean_ms(self):
-        return sum(a.elapsed_time(b) for a, b in self.pairs) / len(self.pairs)
+        if self.whole_step:
+            return self.region[0].elapsed_time(self.region[1]) / self.steps
+        pairs = self.events[:self.used]
+        return sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
+
+
+def c_call(name, *args):
+    """A C-ABI entry point with its arguments marshalled once (tensors become
+    device pointers, plus torch's current stream), for the timed loops; the
+    Python binding of the same name validates the same call during set-up."""
+    f = getattr(mx.lib(), name)
+    conv = [ctypes.c_void_p(a.data_ptr()) if isinstance(a, torch.Tensor) else a for a in args]
+    conv.append(ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+
+    def call():
+        rc = f(*conv)
+        if rc != 0:
+            raise mx.MxError(rc, name)
+    return call
 
 
 # --------------------------------------------------------------------------
@@ -130,11 +187,14 @@ def setup_square(dev, n=16384, fused=True):
     q1 = torch.empty((n, n), dtype=torch.uint8, device=dev)
     b0 = torch.empty((pad(n, 128), pad(n // 32, 4)), dtype=torch.uint8, device=dev)
     b1 = torch.empty_like(b0)
-    timer = Timer()
+    timer = Timer(whole_step=fused)
     if fused:
+        mx.mx_cast_dim0_dim1_blocked(x, out=(q0, b0, q1, b1), raw=True)
+        cast = c_call("mx_cast_dim0_dim1_blocked", x, n, n, q0, b0, q1, b1)
+
         def step():
             with timer:
-                mx.mx_cast_dim0_dim1_blocked(x, out=(q0, b0, q1, b1), raw=True)
+                cast()
 
         # one launch reads X and writes both codes and both blocked scale sets
         kern_bytes = 4 * n * n + 2 * pad(n, 128) * pad(n // 32, 4)
@@ -144,11 +204,17 @@ def setup_square(dev, n=16384, fused=True):
         s0 = torch.empty((n, n // 32), dtype=torch.uint8, device=dev)
         s1 = torch.empty((n, n // 32), dtype=torch.uint8, device=dev)
 
+        mx.mx_cast_dim0_dim1(x, out=(q0, s0, q1, s1), raw=True)
+        mx.mx_scales_to_blocked(s0, out=b0, raw=True)
+        cast = c_call("mx_cast_dim0_dim1", x, n, n, q0, s0, q1, s1)
+        lay0 = c_call("mx_scales_to_blocked", s0, 1, n, n // 32, b0)
+        lay1 = c_call("mx_scales_to_blocked", s1, 1, n, n // 32, b1)
+
         def step():
             with timer:
-                mx.mx_cast_dim0_dim1(x, out=(q0, s0, q1, s1), raw=True)
-            mx.mx_scales_to_blocked(s0, out=b0, raw=True)
-            mx.mx_scales_to_blocked(s1, out=b1, raw=True)
+                cast()
+            lay0()
+            lay1()
 
         kern_bytes = cast_bytes(n, n)
         step_bytes = cast_bytes(n, n) + 2 * blocked_bytes(n, n // 32)
@@ -199,10 +265,15 @@ def setup_moe(dev):
     starts = torch.empty(g + 1, dtype=torch.int64, device=dev)
     timer = Timer()
 
+    mx.mx_cast_dim0_dim1(x, out=(q0, s0, q1, s1), raw=True)
+    mx.mx_scales_to_blocked_grouped(s0, offs, 0, out=out, out_group_starts=starts, raw=True)
+    cast = c_call("mx_cast_dim0_dim1", x, rows, cols, q0, s0, q1, s1)
+    lay = c_call("mx_scales_to_blocked_grouped", s0, rows, cols // 32, offs, g, 0, out, starts)
+
     def step():
         with timer:
-            mx.mx_cast_dim0_dim1(x, out=(q0, s0, q1, s1), raw=True)
-        mx.mx_scales_to_blocked_grouped(s0, offs, 0, out=out, out_group_starts=starts, raw=True)
+            cast()
+        lay()
 
     nb = cast_bytes(rows, cols) + rows * (cols // 32) + out.numel()
     config = {"workload": "mx_cast_dim0_dim1 %dx%d bf16 + M-grouped blocked layout (%d groups)"
@@ -221,14 +292,19 @@ def setup_kgroups(dev):
                       torch.empty(g + 1, dtype=torch.int64, device=dev)))
     timer = Timer()
 
+    calls = []
+    for s, offs, out, starts in items:
+        mx.mx_scales_to_blocked_grouped(s, offs, 1, out=out, out_group_starts=starts, raw=True)
+        calls.append(c_call("mx_scales_to_blocked_grouped", s, s.shape[0], s.shape[1], offs, offs.numel(), 1,
+                            out, starts))
+
     def step():
-        for i, (s, offs, out, starts) in enumerate(items):
+        for i, call in enumerate(calls):
             if i == 1:
                 with timer:
-                    mx.mx_scales_to_blocked_grouped(s, offs, 1, out=out, out_group_starts=starts,
-                                                    raw=True)
+                    call()
             else:
-                mx.mx_scales_to_blocked_grouped(s, offs, 1, out=out, out_group_starts=starts, raw=True)
+                call()
 
     nb = sum(s.numel() + out.numel() for s, _, out, _ in items)
     big = items[1][0].numel() + items[1][2].numel()
@@ -244,11 +320,14 @@ def setup_experts(dev, experts=16, n=8192, k=5120, fused=True):
         w[e] = to_dev_bf16(workloads.expert_weight(e, n, k), dev)
     q = torch.empty((experts, k, n), dtype=torch.uint8, device=dev)
     out = torch.empty((experts, pad(k, 128), pad(n // 32, 4)), dtype=torch.uint8, device=dev)
-    timer = Timer()
+    timer = Timer(whole_step=fused)
     if fused:
+        mx.mx_cast_dim1_3d_blocked(w, out=(q, out), raw=True)
+        cast = c_call("mx_cast_dim1_3d_blocked", w, experts, n, k, q, out)
+
         def step():
             with timer:
-                mx.mx_cast_dim1_3d_blocked(w, out=(q, out), raw=True)
+                cast()
 
         cb = experts * n * k * 3 + out.numel()
         nb = cb
@@ -256,10 +335,15 @@ def setup_experts(dev, experts=16, n=8192, k=5120, fused=True):
     else:
         s = torch.empty((experts, k, n // 32), dtype=torch.uint8, device=dev)
 
+        mx.mx_cast_dim1_3d(w, out=(q, s), raw=True)
+        mx.mx_scales_to_blocked(s, out=out, raw=True)
+        cast = c_call("mx_cast_dim1_3d", w, experts, n, k, q, s)
+        lay = c_call("mx_scales_to_blocked", s, experts, k, n // 32, out)
+
         def step():
             with timer:
-                mx.mx_cast_dim1_3d(w, out=(q, s), raw=True)
-            mx.mx_scales_to_blocked(s, out=out, raw=True)
+                cast()
+            lay()
 
         cb = experts * n * k * 3 + experts * n * k // 32
         nb = cb + blocked_bytes(k, n // 32, experts)
@@ -281,11 +365,14 @@ def setup_rowwise(dev, n=16384):
     x = to_dev_bf16(bits, dev)
     q = torch.empty((n, n), dtype=torch.uint8, device=dev)
     s = torch.empty(n, dtype=torch.int16, device=dev)
-    timer = Timer()
+    timer = Timer(whole_step=True)
+
+    mx.mx_quantize_fp8_rowwise(x, out=(q, s), raw=True)
+    cast = c_call("mx_quantize_fp8_rowwise", x, n, n, q, s)
 
     def step():
         with timer:
-            mx.mx_quantize_fp8_rowwise(x, out=(q, s), raw=True)
+            cast()
 
     nb = 3 * n * n + 2 * n   # read bf16, write e4m3fn, write one bf16 scale per row
 
@@ -313,11 +400,14 @@ def setup_tensorwise(dev, n=16384):
     q = torch.empty((n, n), dtype=torch.uint8, device=dev)
     s = torch.empty(1, dtype=torch.int16, device=dev)
     ws = torch.empty(mx.mx_tensorwise_workspace_bytes(n * n), dtype=torch.uint8, device=dev)
-    timer = Timer()
+    timer = Timer(whole_step=True)
+
+    mx.mx_quantize_fp8_tensorwise(x, out=(q, s), workspace=ws, raw=True)
+    cast = c_call("mx_quantize_fp8_tensorwise", x, n * n, q, s, ws, ws.numel())
 
     def step():
         with timer:
-            mx.mx_quantize_fp8_tensorwise(x, out=(q, s), workspace=ws, raw=True)
+            cast()
 
     # the amax pass must end before any element is converted and the input
     # does not fit on chip: it is read twice (2 + 2 B), codes written (1 B)
@@ -343,7 +433,7 @@ def setup_tensorwise(dev, n=16384):
 def setup_copy(dev, nbytes=1 << 30):
     a = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
     b = torch.empty_like(a)
-    timer = Timer()
+    timer = Timer(whole_step=True)
 
     def step():
         with timer:
@@ -378,18 +468,21 @@ def main():
     mx.lib()
 
     step, step_bytes, timer, kern_bytes, kern_name, cpu_fn, config = WORKLOADS[args.workload](dev)
+    timer.reserve(args.warmup + args.steps)
     torch.cuda.synchronize(dev)
     log("warmup %d steps" % args.warmup)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize(dev)
-    timer.pairs.clear()
+    timer.clear()
 
     log("timing %d steps" % args.steps)
     torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
+    timer.start_region()
     for _ in range(args.steps):
         step()
+    timer.end_region(args.steps)
     torch.cuda.synchronize(dev)
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps

@@ -41,14 +41,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
 
-// Global accesses of the streaming kernels.  They stay ordinary (cached)
-// accesses: non-temporal stores keep the L2 from merging the partial lines
-// that neighbouring lanes and waves write, which multiplies HBM writes.
-__device__ __forceinline__ uint2 load_stream(const uint2* p) { return *p; }
-__device__ __forceinline__ void store_stream(uint4* p, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-  *reinterpret_cast<u32x4*>(p) = (u32x4){a, b, c, d};
+// Store of 16 bytes that, across the lanes of one instruction, make up whole
+// 128-byte lines: non-temporal.  Stores that cover only part of a line stay
+// ordinary (cached) instead: non-temporal ones there keep the L2 from merging
+// the partial lines that neighbouring lanes and workgroups write, which
+// multiplies HBM writes.
+__device__ __forceinline__ void store_line_nt(uint8_t* p, const uint4& v) {
+  __builtin_nontemporal_store((u32x4){v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(p));
 }
-__device__ __forceinline__ void store_stream(uint32_t* p, uint32_t v) { *p = v; }
 
 // Per-half unsigned max of two packed 16-bit pairs (v_pk_max_u16).
 __device__ __forceinline__ uint32_t max2(uint32_t a, uint32_t b) {
