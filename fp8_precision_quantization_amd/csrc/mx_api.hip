@@ -140,7 +140,7 @@ mx_status mx_scales_to_blocked(const uint8_t* s, int64_t batch, int64_t rows, in
     return MX_OK;
   if (out == nullptr || (s == nullptr && rows * cols > 0))
     return MX_ERR_NULL;
-  if ((round_up(rows, 128) / 128) * batch * ((round_up(cols, 4) / 4 + 15) / 16) > kMaxGridBlocks)
+  if (mx::blocked_grid_blocks(0, batch, rows, cols, 1) > kMaxGridBlocks)
     return MX_ERR_SHAPE;
   if (!aligned(out, 16))
     return MX_ERR_ALIGN;
@@ -172,6 +172,8 @@ mx_status mx_scales_to_blocked_grouped(const uint8_t* s, int64_t rows, int64_t c
   if (group_end_offsets == nullptr || (out == nullptr && bytes > 0) ||
       (s == nullptr && rows * cols > 0))
     return MX_ERR_NULL;
+  if (mx::blocked_grid_blocks(group_axis == 0 ? 1 : 2, 1, rows, cols, num_groups) > kMaxGridBlocks)
+    return MX_ERR_SHAPE;
   if (out != nullptr && !aligned(out, 16))
     return MX_ERR_ALIGN;
   if (out_group_starts != nullptr && !aligned(out_group_starts, 8))

@@ -18,6 +18,8 @@ int64_t cast_grid_blocks(int64_t rows, int64_t cols);
 
 hipError_t launch_blocked_batched(const uint8_t* s, int64_t batch, int64_t rows, int64_t cols,
                                   uint8_t* out, hipStream_t stream);
+// Grid of a blocked-layout launch; mode 0 batched, 1 M groups, 2 K groups.
+int64_t blocked_grid_blocks(int32_t mode, int64_t batch, int64_t rows, int64_t cols, int32_t groups);
 hipError_t launch_blocked_grouped(const uint8_t* s, int64_t rows, int64_t cols, const int32_t* ends,
                                   int32_t groups, int32_t axis, uint8_t* out, int64_t out_bytes,
                                   int64_t* out_starts, hipStream_t stream);
