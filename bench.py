@@ -9,8 +9,10 @@ sets written in the 128x4 blocked layout by the same launch.  Other workloads
 (for profiling):
   square16384_3launch  the same result from three launches: the cast with
              plain scales, then mx_scales_to_blocked on each scale set;
-  moe16640   cast of (16640, 5120) activations + M-grouped layout of the row
-             scales (4 groups along M, offsets on the device);
+  moe16640   cast of (16640, 5120) activations writing the row scales in the
+             M-grouped blocked layout itself (4 groups along M, offsets on
+             the device);
+  moe16640_2launch  the same from the plain cast + the M-grouped layout;
   kgroups    K-grouped layouts of (5120, 512), (8192, 4096), (2048, 4096)
              scale tensors (4 groups along K);
   experts16  dim1 cast of (16, 8192, 5120) expert weights with each
@@ -251,34 +253,54 @@ def setup_square_3launch(dev):
     return setup_square(dev, fused=False)
 
 
-def setup_moe(dev):
+def setup_moe(dev, fused=True):
     bits, ends = workloads.moe_activations()
     rows, cols = bits.shape
     x = to_dev_bf16(bits, dev)
     offs = torch.from_numpy(ends).to(dev)
     q0 = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
-    s0 = torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev)
     q1 = torch.empty((cols, rows), dtype=torch.uint8, device=dev)
     s1 = torch.empty((cols, rows // 32), dtype=torch.uint8, device=dev)
     g = len(ends)
     out = torch.empty((rows + 128 * g, pad(cols // 32, 4)), dtype=torch.uint8, device=dev)
     starts = torch.empty(g + 1, dtype=torch.int64, device=dev)
-    timer = Timer()
+    timer = Timer(whole_step=fused)
+    if fused:
+        mx.mx_cast_dim0_dim1_mgrouped(x, offs, out=(q0, out, q1, s1), out_group_starts=starts, raw=True)
+        cast = c_call("mx_cast_dim0_dim1_mgrouped", x, rows, cols, offs, g, q0, out, starts, q1, s1)
 
-    mx.mx_cast_dim0_dim1(x, out=(q0, s0, q1, s1), raw=True)
-    mx.mx_scales_to_blocked_grouped(s0, offs, 0, out=out, out_group_starts=starts, raw=True)
-    cast = c_call("mx_cast_dim0_dim1", x, rows, cols, q0, s0, q1, s1)
-    lay = c_call("mx_scales_to_blocked_grouped", s0, rows, cols // 32, offs, g, 0, out, starts)
+        def step():
+            with timer:
+                cast()
 
-    def step():
-        with timer:
-            cast()
-        lay()
+        # read X; write both code matrices, the grouped row scales, the plain
+        # column scales and the starts
+        kb = rows * cols * 4 + out.numel() + s1.numel() + 8 * (g + 1)
+        nb = kb
+        name = "cast dim0+dim1, M-grouped row scales"
+        label = "mx_cast_dim0_dim1_mgrouped %dx%d bf16, M-grouped blocked row scales (%d groups)"
+    else:
+        s0 = torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev)
+        mx.mx_cast_dim0_dim1(x, out=(q0, s0, q1, s1), raw=True)
+        mx.mx_scales_to_blocked_grouped(s0, offs, 0, out=out, out_group_starts=starts, raw=True)
+        cast = c_call("mx_cast_dim0_dim1", x, rows, cols, q0, s0, q1, s1)
+        lay = c_call("mx_scales_to_blocked_grouped", s0, rows, cols // 32, offs, g, 0, out, starts)
 
-    nb = cast_bytes(rows, cols) + rows * (cols // 32) + out.numel()
-    config = {"workload": "mx_cast_dim0_dim1 %dx%d bf16 + M-grouped blocked layout (%d groups)"
-                          % (rows, cols, g), "rows": rows, "cols": cols, "groups": g}
-    return step, nb, timer, cast_bytes(rows, cols), "cast dim0+dim1", None, config
+        def step():
+            with timer:
+                cast()
+            lay()
+
+        kb = cast_bytes(rows, cols)
+        nb = cast_bytes(rows, cols) + rows * (cols // 32) + out.numel()
+        name = "cast dim0+dim1"
+        label = "mx_cast_dim0_dim1 %dx%d bf16 + M-grouped blocked layout (%d groups)"
+    config = {"workload": label % (rows, cols, g), "rows": rows, "cols": cols, "groups": g}
+    return step, nb, timer, kb, name, None, config
+
+
+def setup_moe_2launch(dev):
+    return setup_moe(dev, fused=False)
 
 
 def setup_kgroups(dev):
@@ -444,7 +466,7 @@ def setup_copy(dev, nbytes=1 << 30):
 
 
 WORKLOADS = {"square16384": setup_square, "square16384_3launch": setup_square_3launch,
-             "moe16640": setup_moe, "kgroups": setup_kgroups, "rowwise16384": setup_rowwise,
+             "moe16640": setup_moe, "moe16640_2launch": setup_moe_2launch, "kgroups": setup_kgroups, "rowwise16384": setup_rowwise,
              "tensorwise16384": setup_tensorwise,
              "experts16": setup_experts, "experts16_2launch": setup_experts_2launch, "copy": setup_copy}
 

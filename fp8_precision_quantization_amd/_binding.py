@@ -33,6 +33,7 @@ SIGNATURES = {
     "mx_cast_dim1_3d": ([_vp, _i64, _i64, _i64, _vp, _vp, _vp], ctypes.c_int),
     "mx_cast_dim0_dim1_blocked": ([_vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "mx_cast_dim1_3d_blocked": ([_vp, _i64, _i64, _i64, _vp, _vp, _vp], ctypes.c_int),
+    "mx_cast_dim0_dim1_mgrouped": ([_vp, _i64, _i64, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "mx_quantize_fp8_rowwise": ([_vp, _i64, _i64, _vp, _vp, _vp], ctypes.c_int),
     "mx_tensorwise_workspace_bytes": ([_i64], _i64),
     "mx_quantize_fp8_tensorwise": ([_vp, _i64, _vp, _vp, _vp, _i64, _vp], ctypes.c_int),
@@ -168,6 +169,43 @@ def mx_cast_dim0_dim1_blocked(x, dim0: bool = True, dim1: bool = True, out=None,
     r0 = _views(q0, s0, raw) if dim0 else (None, None)
     r1 = _views(q1, s1, raw) if dim1 else (None, None)
     return r0[0], r0[1], r1[0], r1[1]
+
+
+def _offsets(offs, name="group_end_offsets"):
+    if not (isinstance(offs, torch.Tensor) and offs.is_cuda and offs.dtype == torch.int32
+            and offs.dim() == 1 and offs.is_contiguous()):
+        raise ValueError("%s must be a contiguous int32 CUDA tensor" % name)
+    return offs
+
+
+def mx_cast_dim0_dim1_mgrouped(x, group_end_offsets, dim1: bool = True, out=None, out_group_starts=None,
+                               raw: bool = False):
+    """MoE activations grouped along M: as mx_cast_dim0_dim1, with the row
+    scales written directly in the M-grouped blocked layout ((R + 128 G,
+    ceil4(C/32)), what mx_scales_to_blocked_grouped(s_row, offsets, 0)
+    gives).  Returns (q_row, s_row_grouped, starts, q_col, s_col); starts is
+    int64 [G + 1] on the device; q_col / s_col are None when dim1 is False."""
+    _bf16_input(x, 2, "x")
+    offs = _offsets(group_end_offsets)
+    rows, cols = x.shape
+    g = offs.numel()
+    o = out if out is not None else (None, None, None, None)
+    q0 = _out(o[0], (rows, cols), x.device, "q_row")
+    s0 = _out(o[1], (rows + 128 * g, _pad(cols // MX_BLOCK, 4)), x.device, "s_row_grouped")
+    q1 = _out(o[2], (cols, rows), x.device, "q_col") if dim1 else None
+    s1 = _out(o[3], (cols, rows // MX_BLOCK), x.device, "s_col") if dim1 else None
+    if out_group_starts is None:
+        starts = torch.empty(g + 1, dtype=torch.int64, device=x.device)
+    else:
+        starts = out_group_starts
+        if starts.dtype != torch.int64 or starts.numel() != g + 1 or not starts.is_contiguous():
+            raise ValueError("out_group_starts must be a contiguous int64 tensor of G + 1")
+    _check(lib().mx_cast_dim0_dim1_mgrouped(_ptr(x), rows, cols, _ptr(offs), g, _ptr(q0), _ptr(s0),
+                                            _ptr(starts), _ptr(q1), _ptr(s1), _stream(x.device)),
+           "mx_cast_dim0_dim1_mgrouped")
+    r0 = _views(q0, s0, raw)
+    r1 = _views(q1, s1, raw) if dim1 else (None, None)
+    return r0[0], r0[1], starts, r1[0], r1[1]
 
 
 def mx_cast_dim1_3d_blocked(w, out=None, raw: bool = False):

@@ -1,6 +1,7 @@
-// C ABI of libmxcast: argument validation on the host, then one launch.
-// Every check runs before any HIP call, so a rejected call enqueues nothing
-// and the checks can be exercised on a machine without a GPU.
+// C ABI of libmxcast: argument validation on the host, then the launches
+// (one per call, three for the tensor-wise cast).  Every check runs before
+// any HIP call, so a rejected call enqueues nothing and the checks can be
+// exercised on a machine without a GPU.
 #include <limits.h>
 
 #include "mx_launch.h"
@@ -83,6 +84,40 @@ mx_status mx_cast_dim0_dim1_blocked(const void* x, int64_t rows, int64_t cols, u
                                       d0 ? q_row : nullptr, d0 ? s_row_blocked : nullptr,
                                       d1 ? q_col : nullptr, d1 ? s_col_blocked : nullptr, true,
                                       stream));
+}
+
+mx_status mx_cast_dim0_dim1_mgrouped(const void* x, int64_t rows, int64_t cols,
+                                     const int32_t* group_end_offsets, int32_t num_groups, uint8_t* q_row,
+                                     uint8_t* s_row_grouped, int64_t* out_group_starts, uint8_t* q_col,
+                                     uint8_t* s_col, hipStream_t stream) {
+  if (rows < 0 || cols < 0 || rows % MX_BLOCK != 0 || cols % MX_BLOCK != 0 || rows > kMaxExtent ||
+      cols > kMaxCastCols)
+    return MX_ERR_SHAPE;
+  if (num_groups < 1 || num_groups > MX_MAX_GROUPS)
+    return MX_ERR_GROUPS;
+  if (rows + 128 * (int64_t)num_groups >= INT_MAX)
+    return MX_ERR_SHAPE;
+  const int64_t bytes = mx_blocked_grouped_bytes(rows, cols / MX_BLOCK, num_groups, 0);
+  if (group_end_offsets == nullptr || (bytes > 0 && s_row_grouped == nullptr))
+    return MX_ERR_NULL;
+  if (!aligned(group_end_offsets, 4) || (s_row_grouped != nullptr && !aligned(s_row_grouped, 16)) ||
+      (out_group_starts != nullptr && !aligned(out_group_starts, 8)))
+    return MX_ERR_ALIGN;
+  if (rows == 0 || cols == 0) {
+    // no codes: the grouped scale buffer is all padding (and the starts)
+    return from_hip(mx::launch_blocked_grouped(nullptr, rows, cols / MX_BLOCK, group_end_offsets, num_groups,
+                                               0, s_row_grouped, bytes, out_group_starts, stream));
+  }
+  const bool d1 = q_col != nullptr || s_col != nullptr;
+  if (x == nullptr || q_row == nullptr || (d1 && (q_col == nullptr || s_col == nullptr)))
+    return MX_ERR_NULL;
+  if (mx::cast_grid_blocks(rows, cols) > kMaxGridBlocks)
+    return MX_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(q_row, 8) || (d1 && !aligned(q_col, 16)))
+    return MX_ERR_ALIGN;
+  return from_hip(mx::launch_cast_mgrouped(static_cast<const uint16_t*>(x), rows, cols, group_end_offsets,
+                                           num_groups, q_row, s_row_grouped, bytes, out_group_starts,
+                                           d1 ? q_col : nullptr, d1 ? s_col : nullptr, stream));
 }
 
 mx_status mx_cast_dim1_3d(const void* w, int64_t experts, int64_t n, int64_t k, uint8_t* q,

@@ -26,6 +26,7 @@
 #include <type_traits>
 
 #include "mx_device.h"
+#include "mx_groups.h"
 #include "mxcast.h"
 #include "mx_launch.h"
 
@@ -39,86 +40,6 @@ constexpr int kTileBytes = 512;
 constexpr int kLdsStride = kStripTiles + 1;  // dwords per staged row (+1 against bank conflicts)
 
 enum : int { kModeBatched = 0, kModeMGroups = 1, kModeKGroups = 2 };
-
-struct GroupTable {
-  int32_t lo[MX_MAX_GROUPS];
-  int32_t hi[MX_MAX_GROUPS];
-  int32_t start[MX_MAX_GROUPS + 1];
-};
-struct NoTable {};
-
-__device__ __forceinline__ int32_t wave_incl_max(int32_t v, int lane) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    int32_t o = __shfl_up(v, d);
-    if (lane >= d)
-      v = max(v, o);
-  }
-  return v;
-}
-
-__device__ __forceinline__ int32_t wave_incl_sum(int32_t v, int lane) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    int32_t o = __shfl_up(v, d);
-    if (lane >= d)
-      v += o;
-  }
-  return v;
-}
-
-// Wave 0 fills the table: end_g = min(max(0, ends_0 .. ends_g), extent),
-// lo_g = end_{g-1} (lo_0 = 0), start_g = sum over h < g of
-// round_up(end_h - lo_h, unit), start_G = padded total.  Lane l handles the
-// groups [l * per, (l + 1) * per).
-__device__ void build_group_table(const int32_t* __restrict__ ends, int groups, int32_t extent,
-                                  int32_t unit, GroupTable& t) {
-  const int lane = threadIdx.x & 63;
-  const int per = (groups + 63) / 64;
-  const int g0 = min(lane * per, groups), g1 = min(g0 + per, groups);
-  int32_t run = 0;
-  for (int g = g0; g < g1; ++g) {
-    run = max(run, ends[g]);
-    t.hi[g] = run;
-  }
-  int32_t incl = wave_incl_max(run, lane);
-  int32_t excl = __shfl_up(incl, 1);
-  if (lane == 0)
-    excl = 0;
-  int32_t prev = min(excl, extent);
-  int32_t local = 0;
-  for (int g = g0; g < g1; ++g) {
-    int32_t e = min(max(excl, t.hi[g]), extent);
-    t.lo[g] = prev;
-    t.hi[g] = e;
-    local += (e - prev + unit - 1) / unit * unit;
-    prev = e;
-  }
-  int32_t sincl = wave_incl_sum(local, lane);
-  int32_t sexcl = sincl - local;
-  for (int g = g0; g < g1; ++g) {
-    t.start[g] = sexcl;
-    sexcl += (t.hi[g] - t.lo[g] + unit - 1) / unit * unit;
-  }
-  int32_t total = __shfl(sincl, 63);
-  if (lane == 0)
-    t.start[groups] = total;
-}
-
-// Last g in [0, groups) with start[g] <= pos, or -1 if pos >= start[groups].
-__device__ __forceinline__ int find_group(const GroupTable& t, int groups, int32_t pos) {
-  if (pos >= t.start[groups])
-    return -1;
-  int lo = 0, hi = groups;  // invariant: start[lo] <= pos < start[hi]
-  while (hi - lo > 1) {
-    int mid = (lo + hi) >> 1;
-    if (t.start[mid] <= pos)
-      lo = mid;
-    else
-      hi = mid;
-  }
-  return lo;
-}
 
 struct Slot {
   int64_t src_col;   // first source column of this tile

@@ -32,8 +32,10 @@
 // ordinary (non-temporal there cost time).
 //
 // With BLK the scales come out directly in the 128x4 blocked layout that
-// grouped GEMMs read (pytorch/ao issue "[mxfp8 moe training] add compile
-// support", the to_blocked layout of the scale tensors): a tile of 128 rows
+// grouped GEMMs read ("[mxfp8 moe training] parallelize along col blocks in
+// scale blocked format kernel for groups along K", Changes: 128x4 is the
+// granularity of the swizzle), as the first page lists among its future
+// improvements (swizzled scales written by the cast): a tile of 128 rows
 // and 256 columns owns two 512-byte blocks of dim0 scales (128 rows x 4
 // scale columns each) and two of dim1 scales (128 columns x 4 row blocks),
 // so each is assembled in LDS and stored as whole 16-byte chunks, the
@@ -42,12 +44,14 @@
 // Workgroups are numbered so that each XCD (workgroups are dispatched
 // round-robin over the 8 XCDs) works on a compact region of the matrix:
 // row_group row tiles side by side, column tiles outermost.  Its L2 then
-// merges the partial lines of the scale matrices, and the region's shape
-// sets how long the contiguous runs of reads and stores are.  The shape and
-// the non-temporal loads were chosen by timing on MI355X.
+// merges the partial lines of the plain scale matrices, and the region's
+// shape sets how long the contiguous runs of reads and stores are.  The
+// shapes (per output form, see cast_args) and the non-temporal loads were
+// chosen by timing on MI355X.
 #include <type_traits>
 
 #include "mx_device.h"
+#include "mx_groups.h"
 #include "mxcast.h"
 #include "mx_launch.h"
 
@@ -106,13 +110,14 @@ __device__ __forceinline__ uint32_t fast_quant4(uint32_t x01, uint32_t x23, uint
 // dim0 of a lane's 16 rows.  rm[i/2] = [row max of row i, row i+1] over the
 // lane's 8 columns; after two DPP moves, the quad's block amax.  Codes: 8 per
 // lane per row (one 256-byte segment per half-wave).  Scale bytes (one per
-// quad): straight to the plain scale matrix, or (BLK) into the LDS image of
-// the tile's two 128x4 blocked tiles at s0_lds + blk_off.
-template <bool SPECIAL, bool BLK>
+// quad): straight to the plain scale matrix (IMG = 0), or into an LDS image
+// of the tile's scales, row i at s0_lds + img_off + i * IMG: the image of the
+// tile's two 128x4 blocked tiles (IMG = 16) or a plain 128 x 8 image (8).
+template <bool SPECIAL, int IMG>
 __device__ __forceinline__ void dim0_rows(const uint4 (&d)[kLaneRows], const uint32_t (&rm)[kLaneRows / 2],
                                           bool quad_leader, __amdgpu_buffer_rsrc_t q0, int q0_off,
                                           __amdgpu_buffer_rsrc_t s0, int s0_off, uint32_t cols,
-                                          uint32_t sb_cols, uint8_t* s0_lds, int blk_off) {
+                                          uint32_t sb_cols, uint8_t* s0_lds, int img_off) {
 #pragma unroll
   for (int i = 0; i < kLaneRows; i += 2) {
     uint32_t m = rm[i / 2];
@@ -140,10 +145,10 @@ __device__ __forceinline__ void dim0_rows(const uint4 (&d)[kLaneRows], const uin
     __builtin_amdgcn_raw_buffer_store_b64((u32x2){qa0, qa1}, q0, q0_off, (int)(i * cols), 0);
     __builtin_amdgcn_raw_buffer_store_b64((u32x2){qb0, qb1}, q0, q0_off, (int)((i + 1) * cols), 0);
     if (quad_leader) {
-      if (BLK) {
-        // rows i, i+1 of the lane are consecutive rows inside a 32-row sub-block
-        s0_lds[blk_off + i * 16] = (uint8_t)ba;
-        s0_lds[blk_off + (i + 1) * 16] = (uint8_t)bb;
+      if (IMG != 0) {
+        // rows i, i+1 of the lane are consecutive rows of the tile
+        s0_lds[img_off + i * IMG] = (uint8_t)ba;
+        s0_lds[img_off + (i + 1) * IMG] = (uint8_t)bb;
       } else {
         __builtin_amdgcn_raw_buffer_store_b8((uint8_t)ba, s0, s0_off, (int)(i * sb_cols), 0);
         __builtin_amdgcn_raw_buffer_store_b8((uint8_t)bb, s0, s0_off, (int)((i + 1) * sb_cols), 0);
@@ -218,6 +223,12 @@ struct CastArgs {
   // segment's dim1 scale matrix, and that matrix's size in bytes.
   int64_t ncb0, ncb1, seg_blk_bytes;
   uint8_t *q0, *s0, *q1, *s1;
+  // M-grouped dim0 scales: group END offsets (device), their count, the
+  // padded starts to write (device, may be null), the output's size in bytes.
+  const int32_t* ends;
+  int32_t groups;
+  int64_t* out_starts;
+  int64_t s0_bytes;
 };
 
 struct Stage {
@@ -243,6 +254,70 @@ __device__ __forceinline__ bool tile_of(uint32_t bid, uint32_t row_tiles, uint32
   return true;
 }
 
+// 4 bytes of dim0 scales (scale columns 4 cb .. 4 cb + 3) of output row o of
+// an M-grouped blocked matrix with ncb column blocks.
+__device__ __forceinline__ void put_row_block(uint8_t* s0, int64_t ncb, int64_t o, int64_t cb, uint32_t v) {
+  const int64_t idx = ((o >> 7) * ncb + cb) * 512 + (o & 31) * 16 + ((o & 127) >> 5) * 4;
+  *reinterpret_cast<uint32_t*>(s0 + idx) = v;
+}
+
+// Store phase of the M-grouped dim0 scales of tile (rt, ct); img holds the
+// tile's scales as 128 rows x 8 bytes.
+__device__ __forceinline__ void mgrouped_scales(const CastArgs& a, const GroupTable& table, const uint8_t* img,
+                                                uint32_t rt, uint32_t ct, int64_t tile_r, int valid_rows) {
+  const int t = threadIdx.x;
+  const int64_t nsc = a.cols / 32;
+  const int64_t cb0 = 2 * (int64_t)ct, cb1 = cb0 + 1;
+  const bool has1 = cb1 < a.ncb0;
+  // scale columns past the matrix are padding: 0
+  const int64_t v0 = min((int64_t)4, nsc - 4 * cb0), v1 = min((int64_t)4, nsc - 4 * cb1);
+  const uint32_t m0 = v0 >= 4 ? 0xFFFFFFFFu : (1u << (8 * v0)) - 1u;
+  const uint32_t m1 = v1 >= 4 ? 0xFFFFFFFFu : v1 <= 0 ? 0u : (1u << (8 * v1)) - 1u;
+  // rows of the tile that belong to a group
+  if (t < valid_rows) {
+    const int64_t r = tile_r + t;
+    const int g = find_source_group(table, a.groups, (int32_t)r);
+    if (g >= 0) {
+      const int64_t o = table.start[g] + (r - table.lo[g]);
+      const uint2 w = reinterpret_cast<const uint2*>(img)[t];
+      put_row_block(a.s0, a.ncb0, o, cb0, w.x & m0);
+      if (has1)
+        put_row_block(a.s0, a.ncb0, o, cb1, w.y & m1);
+    }
+  }
+  // padding rows of the groups whose last row lies in this tile
+  for (int g = find_source_group(table, a.groups, (int32_t)tile_r);
+       g >= 0 && g < a.groups && table.hi[g] <= tile_r + valid_rows; ++g) {
+    if (table.hi[g] == table.lo[g])
+      continue;  // an empty group has no rows and no padding
+    const int64_t o1 = table.start[g + 1];
+    for (int64_t o = table.start[g] + (table.hi[g] - table.lo[g]) + t; o < o1; o += kWaves * 64) {
+      put_row_block(a.s0, a.ncb0, o, cb0, 0u);
+      if (has1)
+        put_row_block(a.s0, a.ncb0, o, cb1, 0u);
+    }
+  }
+  // bytes past the padded total (whole tiles end there): zero, split over
+  // the workgroups of the last row of tiles
+  if (rt == a.row_tiles - 1) {
+    const int64_t lo = (int64_t)table.start[a.groups] * a.ncb0 * 4;   // multiple of 512
+    const int64_t chunk = ((a.s0_bytes - lo + a.col_tiles - 1) / a.col_tiles + 15) / 16 * 16;
+    const int64_t b0 = lo + (int64_t)ct * chunk, b1 = min(a.s0_bytes, b0 + chunk);
+    for (int64_t b = b0 + 16 * t; b < b1; b += 16 * kWaves * 64) {
+      if (b + 16 <= b1) {
+        *reinterpret_cast<uint4*>(a.s0 + b) = make_uint4(0, 0, 0, 0);
+      } else {
+        for (int64_t j = b; j < b1; j += 4)
+          *reinterpret_cast<uint32_t*>(a.s0 + j) = 0u;
+      }
+    }
+  }
+  if (blockIdx.x == 0 && a.out_starts != nullptr) {
+    for (int g = t; g <= a.groups; g += kWaves * 64)
+      a.out_starts[g] = table.start[g];
+  }
+}
+
 // rows_per_seg: the rows of x form consecutive segments of this many rows
 // (3D weights: one per expert; 2D: one segment).  Segment e's dim1 output is
 // a (cols, rows_per_seg) matrix at e * cols * rows_per_seg, its scales a
@@ -252,10 +327,19 @@ __device__ __forceinline__ bool tile_of(uint32_t bid, uint32_t row_tiles, uint32
 // blocked tiles (its 128 rows x 8 scale columns) and its dim1 scales two more
 // (256 matrix rows x 4 scale columns), so every blocked tile, padding
 // included, is written by exactly one workgroup.
-template <bool DIM0, bool DIM1, bool BLK>
+// MGRP (dim0 + plain dim1 only): the dim0 scales are written in the M-grouped
+// blocked layout (the blocked layout of each group of rows, each group
+// padded to a multiple of 128 rows and placed at its padded start; the group
+// table is rebuilt from the device offsets in every workgroup).  Each row's
+// 8 scale bytes of a tile go to its output row as two 4-byte stores; the
+// workgroup holding a group's last row zeroes the group's padding rows, and
+// the last row of tiles zeroes the bytes past the padded total.
+template <bool DIM0, bool DIM1, bool BLK, bool MGRP>
 __global__ __launch_bounds__(256) void cast_kernel(CastArgs a) {
   __shared__ std::conditional_t<DIM1, Stage, NoStage> stage;
-  __shared__ uint8_t s0_blk[(DIM0 && BLK) ? 2 * 512 : 1];
+  // the tile's dim0 scales: two blocked tiles (BLK) or a plain image (MGRP)
+  __shared__ uint8_t s0_blk[(DIM0 && (BLK || MGRP)) ? 2 * 512 : 1];
+  __shared__ std::conditional_t<MGRP, GroupTable, NoTable> table;
 
   uint32_t rt, ct;
   if (!tile_of(blockIdx.x, a.row_tiles, a.col_tiles, a.per_xcd, a.row_group, rt, ct))
@@ -346,18 +430,25 @@ __global__ __launch_bounds__(256) void cast_kernel(CastArgs a) {
           const int s0_off = (int)(half * kLaneRows * sb) + (lc >> 2);
           const bool leader = (lc & 3) == 0;
           // blocked image: tile (lc >> 4), row 16 * half + i of sub-block
-          // `wave`, column (lc >> 2) & 3
-          const int blk_off = (lc >> 4) * 512 + half * 256 + wave * 4 + ((lc >> 2) & 3);
+          // `wave`, column (lc >> 2) & 3; plain image: row 32 * wave + 16 *
+          // half + i, column lc >> 2
+          constexpr int kImg = BLK ? 16 : MGRP ? 8 : 0;
+          const int img_off = BLK ? (lc >> 4) * 512 + half * 256 + wave * 4 + ((lc >> 2) & 3)
+                                  : (wave * kWaveRows + half * kLaneRows) * 8 + (lc >> 2);
           if (any_special)
-            dim0_rows<true, BLK>(d, rm, leader, q0, q0_off, s0, s0_off, (uint32_t)cols, sb, s0_blk, blk_off);
+            dim0_rows<true, kImg>(d, rm, leader, q0, q0_off, s0, s0_off, (uint32_t)cols, sb, s0_blk, img_off);
           else
-            dim0_rows<false, BLK>(d, rm, leader, q0, q0_off, s0, s0_off, (uint32_t)cols, sb, s0_blk, blk_off);
+            dim0_rows<false, kImg>(d, rm, leader, q0, q0_off, s0, s0_off, (uint32_t)cols, sb, s0_blk, img_off);
         }
       }
     }
   }
 
-  if constexpr (DIM1 || (DIM0 && BLK)) {
+  if constexpr (MGRP) {
+    if (wave == 0)
+      build_group_table(a.ends, a.groups, (int32_t)a.rows, kTileRows, table);
+  }
+  if constexpr (DIM1 || (DIM0 && (BLK || MGRP))) {
     // Every wave reaches the barrier; it orders LDS only (no wait on
     // global memory).
     lds_barrier();
@@ -376,6 +467,8 @@ __global__ __launch_bounds__(256) void cast_kernel(CastArgs a) {
       }
     }
   }
+  if constexpr (DIM0 && MGRP)
+    mgrouped_scales(a, table, s0_blk, rt, ct, tile_r, valid_rows);
   if constexpr (DIM1) {
     const Stage& st = stage;
     const int64_t rps = a.rows_per_seg;
@@ -464,6 +557,10 @@ static CastArgs cast_args(const uint16_t* x, int64_t rows, int64_t cols, int64_t
   // that share a plain scale line then run together on one XCD), the
   // dim1-only cast tall ones (all of its stores are col-major).
   a.row_group = q0 != nullptr ? (blocked ? kRowGroupBlocked : kRowGroupPlain) : kRowGroupDim1;
+  a.ends = nullptr;
+  a.groups = 0;
+  a.out_starts = nullptr;
+  a.s0_bytes = 0;
   a.ncb0 = (cols / 32 + 3) / 4;
   a.ncb1 = (rows_per_seg / 32 + 3) / 4;
   a.seg_blk_bytes = (cols + 127) / 128 * 128 * (a.ncb1 * 4);
@@ -477,9 +574,10 @@ int64_t cast_grid_blocks(int64_t rows, int64_t cols) {
   return blocks;
 }
 
-template <bool DIM0, bool DIM1, bool BLK>
+template <bool DIM0, bool DIM1, bool BLK, bool MGRP = false>
 static hipError_t launch_cast(const CastArgs& a, int64_t blocks, hipStream_t stream) {
-  hipLaunchKernelGGL((cast_kernel<DIM0, DIM1, BLK>), dim3((unsigned)blocks), dim3(kWaves * 64), 0, stream, a);
+  hipLaunchKernelGGL((cast_kernel<DIM0, DIM1, BLK, MGRP>), dim3((unsigned)blocks), dim3(kWaves * 64), 0, stream,
+                     a);
   return hipGetLastError();
 }
 
@@ -501,6 +599,20 @@ hipError_t launch_cast_any(const uint16_t* x, int64_t rows, int64_t cols, int64_
   if (d0)
     return launch_cast<true, false, false>(a, blocks, stream);
   return launch_cast<false, true, false>(a, blocks, stream);
+}
+
+hipError_t launch_cast_mgrouped(const uint16_t* x, int64_t rows, int64_t cols, const int32_t* ends,
+                                int32_t groups, uint8_t* q0, uint8_t* s0_grouped, int64_t s0_bytes,
+                                int64_t* out_starts, uint8_t* q1, uint8_t* s1, hipStream_t stream) {
+  int64_t blocks;
+  CastArgs a = cast_args(x, rows, cols, rows, q0, s0_grouped, q1, s1, false, &blocks);
+  a.ends = ends;
+  a.groups = groups;
+  a.out_starts = out_starts;
+  a.s0_bytes = s0_bytes;
+  if (q1 != nullptr)
+    return launch_cast<true, true, false, true>(a, blocks, stream);
+  return launch_cast<true, false, false, true>(a, blocks, stream);
 }
 
 }  // namespace mx

@@ -26,8 +26,9 @@ __device__ __forceinline__ i16x2 as_i16x2(uint32_t v) { return __builtin_bit_cas
 __device__ __forceinline__ uint32_t as_u32(i16x2 v) { return __builtin_bit_cast(uint32_t, v); }
 
 // Workgroup barrier that orders LDS only.  __syncthreads() is a full
-// workgroup fence and waits for every outstanding global load too, which
-// would drain the loads a wave has prefetched for its next tile.
+// workgroup fence: it would also wait for every outstanding global load and
+// store of the wave, which the kernels here want to keep in flight across
+// the barrier.
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();

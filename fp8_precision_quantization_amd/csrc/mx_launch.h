@@ -15,6 +15,11 @@ hipError_t launch_cast_any(const uint16_t* x, int64_t rows, int64_t cols, int64_
                            uint8_t* q0, uint8_t* s0, uint8_t* q1, uint8_t* s1, bool blocked,
                            hipStream_t stream);
 int64_t cast_grid_blocks(int64_t rows, int64_t cols);
+// dim0 + (optional) plain dim1 cast with the dim0 scales in the M-grouped
+// blocked layout (s0_bytes = the grouped output's size).
+hipError_t launch_cast_mgrouped(const uint16_t* x, int64_t rows, int64_t cols, const int32_t* ends,
+                                int32_t groups, uint8_t* q0, uint8_t* s0_grouped, int64_t s0_bytes,
+                                int64_t* out_starts, uint8_t* q1, uint8_t* s1, hipStream_t stream);
 
 hipError_t launch_blocked_batched(const uint8_t* s, int64_t batch, int64_t rows, int64_t cols,
                                   uint8_t* out, hipStream_t stream);

@@ -120,6 +120,35 @@ MX_API mx_status mx_cast_dim0_dim1_blocked(const void* x, int64_t rows, int64_t 
                                            hipStream_t stream);
 
 /*
+ * The same cast for MoE activations grouped along M, with the row scales
+ * written directly in the M-grouped blocked layout -- what
+ * mx_scales_to_blocked_grouped(s_row, ..., group_axis 0) makes of the plain
+ * row scales -- so that the grouped layout needs no pass of its own ("[mxfp8
+ * moe training] add compile support": M-group layout of the (16640, 160)
+ * scales with device-side offsets; "triton kernel to cast to mx across dim0
+ * and dim1", future improvement 2: swizzled scales from the cast).
+ *   group_end_offsets  DEVICE int32 [num_groups], cumulative END rows of the
+ *                      groups (read and clamped on the device exactly as by
+ *                      mx_scales_to_blocked_grouped: undefined result for
+ *                      malformed offsets, but memory-safe).
+ *   s_row_grouped      mx_blocked_grouped_bytes(rows, cols / 32, num_groups,
+ *                      0) bytes, 16-byte aligned; every byte is written.
+ *   out_group_starts   DEVICE int64 [num_groups + 1] or NULL: padded start
+ *                      row of each group, then the padded total.
+ *   q_row              as for mx_cast_dim0_dim1 (required).
+ *   q_col, s_col       plain col-major codes and (cols, rows / 32) scales,
+ *                      as for mx_cast_dim0_dim1, or both NULL (dim0 only).
+ * Shapes as for mx_cast_dim0_dim1; 1 <= num_groups <= MX_MAX_GROUPS (else
+ * MX_ERR_GROUPS) and rows + 128 * num_groups < 2^31.  With rows or cols 0
+ * only the (all-zero) grouped buffer and the starts are written.
+ */
+MX_API mx_status mx_cast_dim0_dim1_mgrouped(const void* x, int64_t rows, int64_t cols,
+                                            const int32_t* group_end_offsets, int32_t num_groups,
+                                            uint8_t* q_row, uint8_t* s_row_grouped,
+                                            int64_t* out_group_starts,
+                                            uint8_t* q_col, uint8_t* s_col, hipStream_t stream);
+
+/*
  * dim1 cast of 3D expert weights, expert by expert.
  *   w  bf16 (experts, n, k) contiguous; 16-byte aligned.
  *   q  e4m3 (experts, k, n): expert e's (n, k) matrix cast in blocks of 32

@@ -33,6 +33,7 @@ def declared_functions():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"mx_status_string", "mx_cast_dim0_dim1", "mx_cast_dim0_dim1_blocked",
+                          "mx_cast_dim0_dim1_mgrouped",
                           "mx_cast_dim1_3d", "mx_cast_dim1_3d_blocked", "mx_quantize_fp8_rowwise",
                           "mx_tensorwise_workspace_bytes", "mx_quantize_fp8_tensorwise",
                           "mx_blocked_bytes", "mx_scales_to_blocked",
@@ -91,6 +92,23 @@ def test_fused_blocked_validation(lib):
     assert g(None, 2, 128, 32, P, P, None) == ERR_NULL
     assert g(P, 2, 128, 32, P, P_ODD, None) == ERR_ALIGN
     assert g(None, 0, 128, 32, None, None, None) == OK
+
+
+def test_mgrouped_cast_validation(lib):
+    f = lib.mx_cast_dim0_dim1_mgrouped
+    assert f(P, 33, 64, P, 4, P, P, P, P, P, None) == ERR_SHAPE
+    assert f(P, 64, 64, P, 0, P, P, P, P, P, None) == ERR_GROUPS
+    assert f(P, 64, 64, P, 1025, P, P, P, P, P, None) == ERR_GROUPS
+    assert f(P, 64, 64, None, 4, P, P, P, P, P, None) == ERR_NULL           # offsets
+    assert f(P, 64, 64, P, 4, P, None, P, P, P, None) == ERR_NULL           # grouped scales
+    assert f(None, 64, 64, P, 4, P, P, P, P, P, None) == ERR_NULL
+    assert f(P, 64, 64, P, 4, None, P, P, P, P, None) == ERR_NULL           # q_row is required
+    assert f(P, 64, 64, P, 4, P, P, P, P, None, None) == ERR_NULL           # half a dim1 pair
+    assert f(P, 64, 64, P, 4, P, ctypes.c_void_p(0x10004), P, P, P, None) == ERR_ALIGN
+    assert f(P, 64, 64, ctypes.c_void_p(0x10002), 4, P, P, P, P, P, None) == ERR_ALIGN
+    assert f(P, 64, 64, P, 4, P, P, ctypes.c_void_p(0x10004), P, P, None) == ERR_ALIGN
+    assert f(P_ODD, 64, 64, P, 4, P, P, P, None, None, None) == ERR_ALIGN
+    assert f(P, (1 << 31) - 128 * 4, 64, P, 4, P, P, P, P, P, None) == ERR_SHAPE
 
 
 def test_rowwise_validation(lib):
