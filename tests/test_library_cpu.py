@@ -186,3 +186,28 @@ def test_python_binding_requires_gpu_tensors():
         mx.mx_cast_dim0_dim1(torch.zeros((32, 32), dtype=torch.bfloat16))
     with pytest.raises(ValueError):
         mx.mx_scales_to_blocked(torch.zeros((4, 4), dtype=torch.uint8))
+
+
+def test_python_binding_rejects_cpu_tensors_everywhere():
+    import torch
+    import fp8_precision_quantization_amd as mx
+    x = torch.zeros((32, 32), dtype=torch.bfloat16)
+    for call in (lambda: mx.mx_cast_dim0_dim1_blocked(x),
+                 lambda: mx.mx_cast_dim1_3d(x.view(1, 32, 32)),
+                 lambda: mx.mx_cast_dim1_3d_blocked(x.view(1, 32, 32)),
+                 lambda: mx.mx_quantize_fp8_rowwise(x),
+                 lambda: mx.mx_quantize_fp8_tensorwise(x),
+                 lambda: mx.mx_cast_dim0_dim1_mgrouped(x, torch.tensor([32], dtype=torch.int32))):
+        with pytest.raises(ValueError):
+            call()
+
+
+def test_missing_library_is_an_error(monkeypatch):
+    """No fallback: without the built library every entry point raises."""
+    from fp8_precision_quantization_amd import _binding
+    monkeypatch.setattr(_binding, "LIB_PATH", "/nonexistent/libmxcast.so")
+    monkeypatch.setattr(_binding, "_lib", None)
+    with pytest.raises(RuntimeError, match="libmxcast.so is missing"):
+        _binding.lib()
+    with pytest.raises(RuntimeError):
+        _binding.mx_blocked_bytes(1, 128, 4)
