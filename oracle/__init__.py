@@ -98,6 +98,12 @@ def _load():
         lib.mxo_quantize_fp8_rowwise.restype = ctypes.c_int
         lib.mxo_quantize_fp8_tensorwise.argtypes = [_u16p, _i64, _u8p, _u16p]
         lib.mxo_quantize_fp8_tensorwise.restype = ctypes.c_int
+        _f64p = ctypes.POINTER(ctypes.c_double)
+        lib.mxo_mx_gemm.argtypes = [_u8p, _u8p, _u8p, _u8p, _i64, _i64, _i64, _f64p, _f64p]
+        lib.mxo_mx_gemm.restype = ctypes.c_int
+        lib.mxo_mx_gemm_grouped.argtypes = [_u8p, _u8p, _u8p, _u8p, _i32p, ctypes.c_int32, _i64, _i64, _i64,
+                                            _f64p, _f64p]
+        lib.mxo_mx_gemm_grouped.restype = ctypes.c_int
         lib.mxo_num_threads.argtypes = []
         lib.mxo_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -245,6 +251,41 @@ def quantize_fp8_tensorwise(bits: np.ndarray):
     _check(_load().mxo_quantize_fp8_tensorwise(_ptr(x.reshape(-1), _u16p), x.size, _ptr(q.reshape(-1), _u8p),
                                                _ptr(s, _u16p)), "quantize_fp8_tensorwise")
     return q, int(s[0])
+
+
+# ---------------------------------------------------------------- MX GEMM
+def _u8(a):
+    return np.ascontiguousarray(a, dtype=np.uint8)
+
+
+def mx_gemm(qa, sa, qb, sb):
+    """C (M, N) fp64 and sum |A B| (M, N) for MX operands: qa (M, K) / sa
+    (M, K/32), qb (N, K) / sb (N, K/32), codes e4m3 and scales e8m0 as uint8."""
+    qa, sa, qb, sb = _u8(qa), _u8(sa), _u8(qb), _u8(sb)
+    m, k = qa.shape
+    n = qb.shape[0]
+    c = np.empty((m, n), np.float64)
+    ab = np.empty((m, n), np.float64)
+    _f64p = ctypes.POINTER(ctypes.c_double)
+    _check(_load().mxo_mx_gemm(_ptr(qa, _u8p), _ptr(sa, _u8p), _ptr(qb, _u8p), _ptr(sb, _u8p), m, n, k,
+                               _ptr(c, _f64p), _ptr(ab, _f64p)), "mx_gemm")
+    return c, ab
+
+
+def mx_gemm_grouped(qa, sa, qb, sb, ends):
+    """Grouped along M: qb (G, N, K), sb (G, N, K/32), ends int32 [G].  Rows
+    past the last (clamped) end are NaN in the result."""
+    qa, sa, qb, sb = _u8(qa), _u8(sa), _u8(qb), _u8(sb)
+    ends = np.ascontiguousarray(ends, dtype=np.int32)
+    m, k = qa.shape
+    g, n, _ = qb.shape
+    c = np.full((m, n), np.nan)
+    ab = np.full((m, n), np.nan)
+    _f64p = ctypes.POINTER(ctypes.c_double)
+    _check(_load().mxo_mx_gemm_grouped(_ptr(qa, _u8p), _ptr(sa, _u8p), _ptr(qb, _u8p), _ptr(sb, _u8p),
+                                       _ptr(ends, _i32p), g, m, n, k, _ptr(c, _f64p), _ptr(ab, _f64p)),
+           "mx_gemm_grouped")
+    return c, ab
 
 
 # ---------------------------------------------------------------- layouts

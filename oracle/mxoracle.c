@@ -36,6 +36,8 @@
  *  - "[float8nocompile]: Triton kernels for conversion to float8 dtypes for
  *    forward pass of Float8LinearNoCompile": the tensor-wise fp8 cast (one
  *    global amax), read at mxo_quantize_fp8_tensorwise below.
+ *  - "[mxfp8 moe training] add compile support", Perf analysis item 1: the
+ *    MXFP8 (grouped) GEMM that consumes the casts, at mxo_mx_gemm below.
  * The pages do not write out the MX scale rule, the rounding mode, the
  * treatment of Inf/NaN or the byte order inside a 128x4 tile.  The readings
  * taken here (each stated at the function that uses it) are:
@@ -563,6 +565,80 @@ int mxo_quantize_fp8_tensorwise(const uint16_t* x, int64_t n, uint8_t* q, uint16
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; ++i)
         q[i] = (uint8_t)mxo_rowwise_element(mxo_bf16_value(x[i]), s);
+    return MXO_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* MX-scaled GEMM: the consumer of the dim0 casts                      */
+/* ------------------------------------------------------------------ */
+/*
+ * Source: "[mxfp8 moe training] add compile support", Perf analysis item 1:
+ * MXFP8 grouped GEMMs on the (16640, 5120) activations grouped along M (4
+ * groups) against per-group (8192, 5120) weights; the operands are the dim0
+ * casts (32-element blocks along K, one e8m0 scale each).  The value an MX
+ * operand stands for is code x 2^(scale byte - 127) (the MX rule above), so
+ * the product is written out as its definition:
+ *   C[m][n] = sum over k of A(m, k) * B(n, k),
+ *   A(m, k) = e4m3(qa[m][k]) * 2^(sa[m][k / 32] - 127), B likewise,
+ * accumulated in fp64 (every product is exact in fp64; the sum is within
+ * rounding of the exact value).  absum[m][n] = sum over k of |A(m, k) B(n, k)|
+ * is returned beside it: it scales the error bound of any faster summation.
+ * A NaN code or a NaN scale byte (0xFF) makes the terms it touches NaN.
+ */
+static double mx_operand(uint8_t code, uint8_t scale)
+{
+    if ((code & 0x7F) == 0x7F || scale == MXO_E8M0_NAN)
+        return NAN;
+    double v = mxo_e4m3_value(code & 0x7F);
+    return ldexp((code & 0x80) ? -v : v, (int)scale - 127);
+}
+
+int mxo_mx_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, const uint8_t* sb, int64_t m,
+                int64_t n, int64_t k, double* c, double* absum)
+{
+    if (m < 0 || n < 0 || k < 0 || k % MXO_BLOCK != 0)
+        return MXO_ERR_ARG;
+    int64_t kb = k / MXO_BLOCK;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < m; ++i) {
+        for (int64_t j = 0; j < n; ++j) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t t = 0; t < k; ++t) {
+                double p = mx_operand(qa[i * k + t], sa[i * kb + t / MXO_BLOCK]) *
+                           mx_operand(qb[j * k + t], sb[j * kb + t / MXO_BLOCK]);
+                acc += p;
+                mag += fabs(p);
+            }
+            c[i * n + j] = acc;
+            if (absum)
+                absum[i * n + j] = mag;
+        }
+    }
+    return MXO_OK;
+}
+
+/* Grouped along M: rows [end_{g-1}, end_g) of A (ends clamped as for the M
+ * groups of the blocked layout) are multiplied by group g's B (n, k) matrix
+ * and scales; rows past the last end are left untouched. */
+int mxo_mx_gemm_grouped(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, const uint8_t* sb,
+                        const int32_t* ends, int32_t groups, int64_t m, int64_t n, int64_t k, double* c,
+                        double* absum)
+{
+    if (groups < 1 || m < 0 || n < 0 || k < 0 || k % MXO_BLOCK != 0)
+        return MXO_ERR_ARG;
+    int64_t lo = 0, kb = k / MXO_BLOCK;
+    for (int32_t g = 0; g < groups; ++g) {
+        int64_t hi = ends[g];
+        if (hi < lo)
+            hi = lo;
+        if (hi > m)
+            hi = m;
+        int rc = mxo_mx_gemm(qa + lo * k, sa + lo * kb, qb + (int64_t)g * n * k, sb + (int64_t)g * n * kb,
+                             hi - lo, n, k, c + lo * n, absum ? absum + lo * n : NULL);
+        if (rc != MXO_OK)
+            return rc;
+        lo = hi;
+    }
     return MXO_OK;
 }
 
