@@ -22,6 +22,9 @@ sets written in the 128x4 blocked layout by the same launch.  Other workloads
              16384 x 16384 input;
   tensorwise16384  the tensor-wise fp8 cast (one bf16 scale, two-stage amax)
              of the same input;
+  gemm16640  the MX-scaled GEMM that consumes the casts: M = 16640, N =
+             8192, K = 5120, bf16 out (TFLOP/s against the MFMA roofline);
+  ggemm16640 the same grouped along M (4 groups, per-group weights);
   copy       a plain device-to-device copy of 1 GiB (counter calibration).
 
 Each workload's calls are validated once through the Python binding; the
@@ -55,6 +58,7 @@ import fp8_precision_quantization_amd as mx  # noqa: E402
 from fp8_precision_quantization_amd import workloads  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+MFMA_FP8_PEAK_TFLOPS = 5000.0   # dense fp8 MFMA, MI355X
 METRIC = "achieved HBM GB/s (% of MI355X peak) for bf16→MXFP8 dim0+dim1 cast"
 CAST_SOURCES = ["fp8_precision_quantization_amd/csrc/mx_cast.hip",
                 "fp8_precision_quantization_amd/csrc/mx_device.h"]
@@ -452,6 +456,53 @@ def setup_tensorwise(dev, n=16384):
     return step, nb, timer, nb, "tensor-wise fp8 cast (amax + cast launches)", cpu_baseline, config
 
 
+def _mx_operands(rows, k, seed, dev):
+    """Seeded random finite e4m3 codes and e8m0 scales (2^-9 .. 2^8)."""
+    rng = np.random.default_rng(seed)
+    q = rng.integers(0, 256, size=(rows, k), dtype=np.uint8)
+    q[(q & 0x7F) == 0x7F] = 0x7E
+    s = rng.integers(118, 136, size=(rows, k // 32), dtype=np.uint8)
+    return torch.from_numpy(q).to(dev), torch.from_numpy(s).to(dev)
+
+
+def setup_gemm(dev, grouped=False, m=16640, n=8192, k=5120):
+    log("generating MX operands")
+    qa, sa = _mx_operands(m, k, 101, dev)
+    if grouped:
+        _, ends = workloads.moe_activations()
+        g = len(ends)
+        ops = [_mx_operands(n, k, 200 + i, dev) for i in range(g)]
+        qb = torch.stack([o[0] for o in ops])
+        sb = torch.stack([o[1] for o in ops])
+        offs = torch.from_numpy(ends).to(dev)
+    else:
+        qb, sb = _mx_operands(n, k, 102, dev)
+    c = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    timer = Timer(whole_step=True)
+    if grouped:
+        mx.mx_grouped_gemm_mxfp8(qa, sa, qb, sb, offs, out=c)
+        call = c_call("mx_grouped_gemm_mxfp8", qa, sa, qb, sb, offs, g, m, n, k, c, 1)
+    else:
+        mx.mx_gemm_mxfp8(qa, sa, qb, sb, out=c)
+        call = c_call("mx_gemm_mxfp8", qa, sa, qb, sb, m, n, k, c, 1)
+
+    def step():
+        with timer:
+            call()
+
+    flops = 2 * m * n * k
+    config = {"workload": "%s M=%d N=%d K=%d, e4m3 x e4m3 with e8m0 block scales, bf16 out%s"
+                          % ("mx_grouped_gemm_mxfp8" if grouped else "mx_gemm_mxfp8", m, n, k,
+                             ", 4 groups along M" if grouped else ""),
+              "m": m, "n": n, "k": k, "unit": "TFLOP/s", "bound": "mfma", "peak": MFMA_FP8_PEAK_TFLOPS,
+              "flops": flops}
+    return step, flops, timer, flops, "MX GEMM" + (" grouped" if grouped else ""), None, config
+
+
+def setup_ggemm(dev):
+    return setup_gemm(dev, grouped=True)
+
+
 def setup_copy(dev, nbytes=1 << 30):
     a = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
     b = torch.empty_like(a)
@@ -467,7 +518,7 @@ def setup_copy(dev, nbytes=1 << 30):
 
 WORKLOADS = {"square16384": setup_square, "square16384_3launch": setup_square_3launch,
              "moe16640": setup_moe, "moe16640_2launch": setup_moe_2launch, "kgroups": setup_kgroups, "rowwise16384": setup_rowwise,
-             "tensorwise16384": setup_tensorwise,
+             "tensorwise16384": setup_tensorwise, "gemm16640": setup_gemm, "ggemm16640": setup_ggemm,
              "experts16": setup_experts, "experts16_2launch": setup_experts_2launch, "copy": setup_copy}
 
 
@@ -508,24 +559,27 @@ def main():
     torch.cuda.synchronize(dev)
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    scale = 1e12 if config.get("unit") == "TFLOP/s" else 1e9
+    unit = config.pop("unit", "GB/s")
+    bound = config.pop("bound", "hbm")
+    peak = config.pop("peak", HBM_PEAK_GBS)
+    value = step_bytes / (ms_per_step * 1e-3) / scale
     kern_ms = timer.mean_ms()
-    achieved = kern_bytes / (kern_ms * 1e-3) / 1e9
-    log("step %.2f us, %s %.2f us = %.1f GB/s" % (ms_per_step * 1e3, kern_name, kern_ms * 1e3,
-                                                  achieved))
+    achieved = kern_bytes / (kern_ms * 1e-3) / scale
+    log("step %.2f us, %s %.2f us = %.1f %s" % (ms_per_step * 1e3, kern_name, kern_ms * 1e3, achieved, unit))
 
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4),
+    roofline = {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4),
                 "traffic": counter_traffic() if args.workload == "square16384" else None,
                 "kernel": kern_name, "kernel_us": round(kern_ms * 1e3, 2),
-                "algorithmic_bytes": kern_bytes}
+                ("algorithmic_flops" if unit == "TFLOP/s" else "algorithmic_bytes"): kern_bytes}
 
     cpu = None
     if cpu_fn is not None and not args.no_cpu_baseline:
         log("timing the CPU oracle on a slice")
         cpu = cpu_fn()
 
-    line = {"metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+    line = {"metric": METRIC, "value": round(value, 1), "unit": unit, "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
             "data": "synthetic", "config": config, "roofline": roofline, "cpu_baseline": cpu}

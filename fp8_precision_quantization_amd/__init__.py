@@ -15,6 +15,8 @@ from ._binding import (  # noqa: F401
     mx_cast_dim0_dim1_mgrouped,
     mx_cast_dim1_3d,
     mx_cast_dim1_3d_blocked,
+    mx_gemm_mxfp8,
+    mx_grouped_gemm_mxfp8,
     mx_quantize_fp8_rowwise,
     mx_quantize_fp8_tensorwise,
     mx_scales_to_blocked,

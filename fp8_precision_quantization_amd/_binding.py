@@ -37,6 +37,8 @@ SIGNATURES = {
     "mx_quantize_fp8_rowwise": ([_vp, _i64, _i64, _vp, _vp, _vp], ctypes.c_int),
     "mx_tensorwise_workspace_bytes": ([_i64], _i64),
     "mx_quantize_fp8_tensorwise": ([_vp, _i64, _vp, _vp, _vp, _i64, _vp], ctypes.c_int),
+    "mx_gemm_mxfp8": ([_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _i32, _vp], ctypes.c_int),
+    "mx_grouped_gemm_mxfp8": ([_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _i32, _vp], ctypes.c_int),
     "mx_blocked_bytes": ([_i64, _i64, _i64], _i64),
     "mx_scales_to_blocked": ([_vp, _i64, _i64, _i64, _vp, _vp], ctypes.c_int),
     "mx_blocked_grouped_bytes": ([_i64, _i64, _i32, _i32], _i64),
@@ -280,6 +282,55 @@ def mx_quantize_fp8_tensorwise(x, out=None, workspace=None, raw: bool = False):
     if raw:
         return q, s.view(torch.int16)
     return q.view(torch.float8_e4m3fn), s.view(torch.bfloat16)
+
+
+def _mx_operand(q, s, rows, k, name):
+    q = _scale_input(q, name + " codes")
+    s = _scale_input(s, name + " scales")
+    if tuple(q.shape[-2:]) != (rows, k) or tuple(s.shape[-2:]) != (rows, k // MX_BLOCK):
+        raise ValueError("%s: codes (%d, %d) and scales (%d, %d) expected" % (name, rows, k, rows, k // MX_BLOCK))
+    return q, s
+
+
+def _gemm_out(out, shape, out_dtype, device):
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("out_dtype must be float32 or bfloat16")
+    if out is None:
+        return torch.empty(shape, dtype=out_dtype, device=device)
+    if out.dtype != out_dtype or tuple(out.shape) != tuple(shape) or not out.is_contiguous() or out.device != device:
+        raise ValueError("out must be a contiguous %s %s tensor on %s" % (out_dtype, tuple(shape), device))
+    return out
+
+
+def mx_gemm_mxfp8(qa, sa, qb, sb, out_dtype=torch.bfloat16, out=None):
+    """C (M, N) = A @ B^T for MX operands: qa (M, K) e4m3 codes with sa (M,
+    K/32) e8m0 scales, qb (N, K) with sb (N, K/32) -- the dim0 casts' outputs."""
+    m, k = qa.shape
+    n = qb.shape[0]
+    qa, sa = _mx_operand(qa, sa, m, k, "A")
+    qb, sb = _mx_operand(qb, sb, n, k, "B")
+    c = _gemm_out(out, (m, n), out_dtype, qa.device)
+    _check(lib().mx_gemm_mxfp8(_ptr(qa), _ptr(sa), _ptr(qb), _ptr(sb), m, n, k, _ptr(c),
+                               int(out_dtype == torch.bfloat16), _stream(qa.device)), "mx_gemm_mxfp8")
+    return c
+
+
+def mx_grouped_gemm_mxfp8(qa, sa, qb, sb, group_end_offsets, out_dtype=torch.bfloat16, out=None):
+    """Grouped along M: rows of group g of A times group g's weights, qb (G,
+    N, K) / sb (G, N, K/32); offsets int32 [G] on the device.  Rows past the
+    last end are left as they were in `out`."""
+    m, k = qa.shape
+    g, n, _ = qb.shape
+    offs = _offsets(group_end_offsets)
+    if offs.numel() != g:
+        raise ValueError("one offset per group of B")
+    qa, sa = _mx_operand(qa, sa, m, k, "A")
+    qb, sb = _mx_operand(qb, sb, n, k, "B")
+    c = _gemm_out(out, (m, n), out_dtype, qa.device)
+    _check(lib().mx_grouped_gemm_mxfp8(_ptr(qa), _ptr(sa), _ptr(qb), _ptr(sb), _ptr(offs), g, m, n, k, _ptr(c),
+                                       int(out_dtype == torch.bfloat16), _stream(qa.device)),
+           "mx_grouped_gemm_mxfp8")
+    return c
 
 
 def mx_blocked_bytes(batch: int, rows: int, cols: int) -> int:

@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmxcast.so")
-SOURCES = ["mx_api.hip", "mx_cast.hip", "mx_blocked.hip", "mx_rowwise.hip", "mx_tensorwise.hip"]
+SOURCES = ["mx_api.hip", "mx_cast.hip", "mx_blocked.hip", "mx_rowwise.hip", "mx_tensorwise.hip", "mx_gemm.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

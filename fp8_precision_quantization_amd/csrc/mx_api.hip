@@ -15,11 +15,29 @@ constexpr int64_t kMaxExtent = (int64_t)1 << 40;  // per-dimension bound, keeps 
 constexpr int64_t kMaxCastCols = (int64_t)1 << 25;
 constexpr int64_t kMaxGridBlocks = INT_MAX;
 constexpr int64_t kMaxRowwiseCols = (int64_t)1 << 30;
+// The GEMM addresses a wave's 64 operand rows from one base with 32-bit
+// offsets: 64 * k bytes must stay below 2^31.
+constexpr int64_t kMaxGemmK = (int64_t)1 << 24;
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
 mx_status from_hip(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_HIP; }
+
+mx_status check_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, const uint8_t* sb, int64_t m,
+                     int64_t n, int64_t k, const void* c, int32_t c_bf16) {
+  if (m < 0 || n < 0 || k < 0 || k % MX_BLOCK != 0 || m >= INT_MAX || n >= INT_MAX || k > kMaxGemmK)
+    return MX_ERR_SHAPE;
+  if (c_bf16 != 0 && c_bf16 != 1)
+    return MX_ERR_SHAPE;
+  if (m == 0 || n == 0)
+    return MX_OK;
+  if (c == nullptr || (k > 0 && (qa == nullptr || sa == nullptr || qb == nullptr || sb == nullptr)))
+    return MX_ERR_NULL;
+  if (!aligned(qa, 16) || !aligned(qb, 16) || !aligned(c, c_bf16 ? 2 : 4))
+    return MX_ERR_ALIGN;
+  return MX_OK;
+}
 
 }  // namespace
 
@@ -258,6 +276,36 @@ mx_status mx_quantize_fp8_tensorwise(const void* x, int64_t n, uint8_t* q, uint1
     return MX_ERR_SHAPE;
   return from_hip(mx::launch_tensorwise(static_cast<const uint16_t*>(x), n, q, scale,
                                         static_cast<uint32_t*>(workspace), vec, stream));
+}
+
+mx_status mx_gemm_mxfp8(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, const uint8_t* sb, int64_t m,
+                        int64_t n, int64_t k, void* c, int32_t c_bf16, hipStream_t stream) {
+  const mx_status st = check_gemm(qa, sa, qb, sb, m, n, k, c, c_bf16);
+  if (st != MX_OK || m == 0 || n == 0)
+    return st;
+  if (mx::gemm_grid_blocks(m, n, false, 0) > kMaxGridBlocks)
+    return MX_ERR_SHAPE;
+  return from_hip(mx::launch_mx_gemm(qa, sa, qb, sb, m, n, k, c, c_bf16 != 0, nullptr, 0, stream));
+}
+
+mx_status mx_grouped_gemm_mxfp8(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, const uint8_t* sb,
+                                const int32_t* group_end_offsets, int32_t num_groups, int64_t m, int64_t n,
+                                int64_t k, void* c, int32_t c_bf16, hipStream_t stream) {
+  if (num_groups < 1 || num_groups > MX_MAX_GROUPS)
+    return MX_ERR_GROUPS;
+  const mx_status st = check_gemm(qa, sa, qb, sb, m, n, k, c, c_bf16);
+  if (st != MX_OK || m == 0 || n == 0)
+    return st;
+  if (m + 128 * (int64_t)num_groups >= INT_MAX)
+    return MX_ERR_SHAPE;
+  if (group_end_offsets == nullptr)
+    return MX_ERR_NULL;
+  if (!aligned(group_end_offsets, 4))
+    return MX_ERR_ALIGN;
+  if (mx::gemm_grid_blocks(m, n, true, num_groups) > kMaxGridBlocks)
+    return MX_ERR_SHAPE;
+  return from_hip(
+      mx::launch_mx_gemm(qa, sa, qb, sb, m, n, k, c, c_bf16 != 0, group_end_offsets, num_groups, stream));
 }
 
 }  // extern "C"

@@ -21,6 +21,9 @@
  *  - "[float8nocompile]: Triton kernels for conversion to float8 dtypes for
  *    forward pass of Float8LinearNoCompile": the tensor-wise fp8 cast with a
  *    two-stage global amax (mx_quantize_fp8_tensorwise).
+ *  - "[mxfp8 moe training] add compile support", Perf analysis item 1: the
+ *    MXFP8 (grouped) GEMM that consumes the casts (mx_gemm_mxfp8,
+ *    mx_grouped_gemm_mxfp8).
  *
  * MX rule (the pages do not spell it out; this is the reading implemented):
  *   amax  = max |x| over a block of 32 (NaN > +Inf > finite);
@@ -275,6 +278,41 @@ MX_API int64_t mx_tensorwise_workspace_bytes(int64_t n);
 MX_API mx_status mx_quantize_fp8_tensorwise(const void* x, int64_t n, uint8_t* q, uint16_t* scale,
                                             void* workspace, int64_t workspace_bytes,
                                             hipStream_t stream);
+
+/*
+ * MX-scaled GEMM, the consumer of the dim0 casts ("[mxfp8 moe training] add
+ * compile support", Perf analysis item 1: MXFP8 grouped GEMMs of the MoE
+ * activations against per-group weights), on gfx950's block-scaled MFMA:
+ *   C[m][n] = sum over k of A(m, k) * B(n, k), with
+ *   A(m, k) = e4m3(qa[m][k]) * 2^(sa[m][k / 32] - 127) and B likewise.
+ *   qa, sa   A codes (m, k) and scales (m, k / 32) as mx_cast_dim0_dim1
+ *            writes q_row / s_row; qa 16-byte aligned.
+ *   qb, sb   B codes (n, k) and scales (n, k / 32), K-major the same way
+ *            (the dim0 cast of a (n, k) weight); qb 16-byte aligned.
+ *   c        (m, n) row-major: binary32 (c_bf16 = 0, 4-byte aligned) or bf16
+ *            rounded to nearest-even (c_bf16 = 1, 2-byte aligned).
+ * The products of each 64-deep K step are summed by the MFMA with less than
+ * binary32 precision (measured on MI355X: within 3.4e-4 of the step's
+ * largest product); the steps accumulate in binary32.  A NaN code or scale
+ * (0xFF) gives NaN where it enters.
+ * m, n, k >= 0, k % 32 == 0, k <= 2^24, m, n < 2^31, else MX_ERR_SHAPE; m or
+ * n 0 writes nothing; k 0 writes zeros.
+ */
+MX_API mx_status mx_gemm_mxfp8(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, const uint8_t* sb,
+                               int64_t m, int64_t n, int64_t k, void* c, int32_t c_bf16, hipStream_t stream);
+
+/*
+ * The same GEMM grouped along M: rows [end_{g-1}, end_g) of A (cumulative
+ * END offsets on the device, clamped as by mx_scales_to_blocked_grouped)
+ * are multiplied by group g's weights, qb / sb holding num_groups
+ * consecutive (n, k) / (n, k / 32) matrices.  Rows past the last end are
+ * not written.  1 <= num_groups <= MX_MAX_GROUPS (else MX_ERR_GROUPS), m +
+ * 128 * num_groups < 2^31; other arguments as for mx_gemm_mxfp8.
+ */
+MX_API mx_status mx_grouped_gemm_mxfp8(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb,
+                                       const uint8_t* sb, const int32_t* group_end_offsets,
+                                       int32_t num_groups, int64_t m, int64_t n, int64_t k, void* c,
+                                       int32_t c_bf16, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -36,6 +36,7 @@ def test_exports_every_declared_symbol(lib):
                           "mx_cast_dim0_dim1_mgrouped",
                           "mx_cast_dim1_3d", "mx_cast_dim1_3d_blocked", "mx_quantize_fp8_rowwise",
                           "mx_tensorwise_workspace_bytes", "mx_quantize_fp8_tensorwise",
+                          "mx_gemm_mxfp8", "mx_grouped_gemm_mxfp8",
                           "mx_blocked_bytes", "mx_scales_to_blocked",
                           "mx_blocked_grouped_bytes", "mx_scales_to_blocked_grouped"}
     for n in names:
@@ -109,6 +110,24 @@ def test_mgrouped_cast_validation(lib):
     assert f(P, 64, 64, P, 4, P, P, ctypes.c_void_p(0x10004), P, P, None) == ERR_ALIGN
     assert f(P_ODD, 64, 64, P, 4, P, P, P, None, None, None) == ERR_ALIGN
     assert f(P, (1 << 31) - 128 * 4, 64, P, 4, P, P, P, P, P, None) == ERR_SHAPE
+
+
+def test_gemm_validation(lib):
+    f = lib.mx_gemm_mxfp8
+    assert f(P, P, P, P, 64, 64, 48, P, 0, None) == ERR_SHAPE        # k not a multiple of 32
+    assert f(P, P, P, P, -1, 64, 64, P, 0, None) == ERR_SHAPE
+    assert f(P, P, P, P, 64, 64, (1 << 24) + 32, P, 0, None) == ERR_SHAPE
+    assert f(P, P, P, P, 64, 64, 64, P, 2, None) == ERR_SHAPE        # output type
+    assert f(None, None, None, None, 0, 64, 64, None, 0, None) == OK
+    assert f(P, P, None, P, 64, 64, 64, P, 0, None) == ERR_NULL
+    assert f(P, P, P, P, 64, 64, 64, None, 0, None) == ERR_NULL
+    assert f(P_ODD, P, P, P, 64, 64, 64, P, 0, None) == ERR_ALIGN
+    assert f(P, P, P, P, 64, 64, 64, ctypes.c_void_p(0x10002), 0, None) == ERR_ALIGN   # fp32 needs 4
+    g = lib.mx_grouped_gemm_mxfp8
+    assert g(P, P, P, P, P, 0, 64, 64, 64, P, 1, None) == ERR_GROUPS
+    assert g(P, P, P, P, None, 2, 64, 64, 64, P, 1, None) == ERR_NULL
+    assert g(P, P, P, P, ctypes.c_void_p(0x10002), 2, 64, 64, 64, P, 1, None) == ERR_ALIGN
+    assert g(P, P, P, P, P, 2, (1 << 31) - 200, 64, 64, P, 1, None) == ERR_SHAPE
 
 
 def test_rowwise_validation(lib):
