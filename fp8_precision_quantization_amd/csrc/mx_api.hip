@@ -17,7 +17,7 @@ constexpr int64_t kMaxGridBlocks = INT_MAX;
 constexpr int64_t kMaxRowwiseCols = (int64_t)1 << 30;
 // The GEMM addresses a wave's 64 operand rows from one base with 32-bit
 // offsets: 64 * k bytes must stay below 2^31.
-constexpr int64_t kMaxGemmK = (int64_t)1 << 24;
+constexpr int64_t kMaxGemmK = (int64_t)1 << 23;
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
@@ -296,7 +296,7 @@ mx_status mx_grouped_gemm_mxfp8(const uint8_t* qa, const uint8_t* sa, const uint
   const mx_status st = check_gemm(qa, sa, qb, sb, m, n, k, c, c_bf16);
   if (st != MX_OK || m == 0 || n == 0)
     return st;
-  if (m + 128 * (int64_t)num_groups >= INT_MAX)
+  if (m + 256 * (int64_t)num_groups >= INT_MAX)
     return MX_ERR_SHAPE;
   if (group_end_offsets == nullptr)
     return MX_ERR_NULL;

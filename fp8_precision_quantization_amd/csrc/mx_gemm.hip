@@ -19,17 +19,28 @@
 // (measured: within 3.4e-4 of the largest product of the step); the fp32
 // accumulator carries the sum across steps.
 //
-// Work decomposition: a 256-thread workgroup owns a 128 x 128 tile of C;
-// wave w its (w / 2, w % 2) 64 x 64 quadrant = 2 x 2 MFMA blocks.  Operands
-// go straight from memory to registers in the MFMA layout (two 16-byte
-// buffer loads per 32-row slab per lane), double-buffered so that the loads
-// of the next K step are in flight while the current one multiplies.  Buffer
-// ranges end at the tile's last row, so rows past M or N read as zero.
-// Workgroups are numbered so that each XCD works on a compact block of
-// tiles, whose A rows and B columns then stay in its L2.
+// Work decomposition: a 256-thread workgroup owns a 256 x 256 tile of C;
+// wave w its (w / 2, w % 2) 128 x 128 quarter = 4 x 4 MFMA blocks, whose
+// 256 accumulators live in the accumulation registers.  K advances in
+// stages of 128 bytes: the workgroup loads the stage's 256 rows of A and of
+// B (32 KiB each; every load instruction reads 32 whole 128-byte rows) into
+// registers while the MFMAs work on the previous stage, then writes them to
+// the other half of a double-buffered LDS area.  Each wave reads its MFMA
+// operands from LDS with 16-byte reads.  In LDS a row's eight 16-byte chunks
+// are permuted by an XOR of the row index (f below), so that the 16 lanes
+// of one LDS read phase, which read one chunk of 16 consecutive rows, hit
+// distinct banks, as do the writes.  Scales go straight to registers: one
+// dword (the row's four blocks of the stage) per row slab and lane.
+//
+// Buffer ranges end at the tile's last row, so rows past M or N read as
+// zero; chunks past K are not loaded (zero), and their blocks take scale 1.
+// Tiles are ordered in bands of 8 tile rows, column by column, and the
+// ordered list is cut into 8 contiguous pieces, one per XCD (workgroups are
+// dealt to the XCDs round-robin), so that each XCD's L2 sees a compact
+// region of A rows and B columns.
 //
 // Grouped along M (GROUPED): the tiles of group g cover its rows [lo_g,
-// hi_g) in 128-row steps from the group's padded start (the group table of
+// hi_g) in 256-row steps from the group's padded start (the group table of
 // the blocked layouts, rebuilt from the device offsets in each workgroup);
 // B and its scales are group g's (N, K) slice.  Rows past the last end are
 // not written.
@@ -44,10 +55,14 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kGemmThreads = 256;
-constexpr int kGemmTile = 128;      // rows and columns of C per workgroup
-constexpr int kGemmStep = 64;       // K per MFMA
-constexpr int kGemmXcdBlock = 8;    // tiles per side of an XCD's block of C
-constexpr uint32_t kE8m0One = 127;  // e8m0 byte of 2^0
+constexpr int kGemmTile = 256;                 // rows and columns of C per workgroup
+constexpr int kGemmTK = 128;                   // K bytes per LDS stage
+constexpr int kGemmWaveBlocks = 4;             // 32 x 32 MFMA blocks per wave along M and along N
+constexpr int kGemmLoadRows = kGemmThreads * 16 / kGemmTK;   // rows per load instruction (32)
+constexpr int kGemmLoads = kGemmTile / kGemmLoadRows;        // load instructions per operand and stage (8)
+constexpr int kGemmStageBytes = kGemmTile * kGemmTK;         // one operand's stage (32 KiB)
+constexpr int kGemmBand = 8;                   // tile rows per band of the tile order
+constexpr uint32_t kE8m0One = 127;             // e8m0 byte of 2^0
 
 struct GemmArgs {
   const uint8_t *qa, *sa, *qb, *sb;
@@ -56,48 +71,15 @@ struct GemmArgs {
   const int32_t* ends;
   int32_t groups;
   uint32_t tiles_m, tiles_n;   // tile grid (tiles_m includes one spare tile per group when grouped)
-  uint32_t items;              // work items: whole kGemmXcdBlock^2 blocks of tiles
-  uint32_t per_xcd;            // work items per XCD
+  uint32_t per_xcd;            // tiles per XCD
 };
 
-struct Operands {
-  v8i a[2], b[2];
-  int sa[2], sb[2];
-};
-
-// One 32-row slab of an operand for K step k0: the lane's row at row_off
-// (bytes, within the tile), bytes 16 (l / 32) .. + 15 of both 32-blocks.
-// A step past K (the half block of a K that is 32 mod 64) reads as zero.
-__device__ __forceinline__ v8i load_slab(__amdgpu_buffer_rsrc_t rs, int row_off, int k0, bool second_ok) {
-  const u32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(rs, row_off, k0, 0);
-  u32x4 hi = {0, 0, 0, 0};
-  if (second_ok)
-    hi = __builtin_amdgcn_raw_buffer_load_b128(rs, row_off, k0 + 32, 0);
-  return (v8i){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-}
-
-__device__ __forceinline__ void load_step(Operands& o, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rsa,
-                                          __amdgpu_buffer_rsrc_t rb, __amdgpu_buffer_rsrc_t rsb,
-                                          const int (&a_off)[2], const int (&b_off)[2], const int (&sa_off)[2],
-                                          const int (&sb_off)[2], int k0, bool second_ok, bool my_block_ok) {
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    o.a[i] = load_slab(ra, a_off[i], k0, second_ok);
-    o.b[i] = load_slab(rb, b_off[i], k0, second_ok);
-    // this lane's scale: block (l / 32) of the step; a block past K gets
-    // scale 1 (its data is zero)
-    o.sa[i] = my_block_ok ? (int)__builtin_amdgcn_raw_buffer_load_b8(rsa, sa_off[i], k0 / 32, 0) : (int)kE8m0One;
-    o.sb[i] = my_block_ok ? (int)__builtin_amdgcn_raw_buffer_load_b8(rsb, sb_off[i], k0 / 32, 0) : (int)kE8m0One;
-  }
-}
-
-__device__ __forceinline__ void mma_step(v16f (&acc)[2][2], const Operands& o) {
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(o.a[i], o.b[j], acc[i][j], 0, 0, 0, o.sa[i], 0,
-                                                                  o.sb[j]);
+// Position of 16-byte chunk c of a stage row in LDS (bytes from the
+// operand's stage base).  The XOR keeps a read of one chunk by 16
+// consecutive rows, and a write of a row's 8 chunks by 8 lanes, on
+// distinct banks.
+__device__ __forceinline__ int lds_chunk(int row, int c) {
+  return row * kGemmTK + 16 * (c ^ ((row & 7) ^ ((row >> 3) & 1)));
 }
 
 // binary32 -> bf16 bits, nearest-even; NaN -> 0x7FC0.
@@ -108,25 +90,41 @@ __device__ __forceinline__ uint16_t to_bf16(float f) {
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
-template <bool GROUPED, bool BF16>
+// The four block scales (bytes) of the stage at K offset kt for the row
+// whose scales start at row_off (bytes) in rs.  DW: the row's scales are
+// dword-aligned (K % 128 == 0) and the stage lies inside K.
+template <bool DW>
+__device__ __forceinline__ uint32_t stage_scales(__amdgpu_buffer_rsrc_t rs, int row_off, int kt, int64_t kb) {
+  if (DW)
+    return __builtin_amdgcn_raw_buffer_load_b32(rs, row_off, kt / 32, 0);
+  uint32_t w = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int blk = kt / 32 + b;
+    const uint32_t v = blk < kb ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs, row_off, blk, 0) : kE8m0One;
+    w |= v << (8 * b);
+  }
+  return w;
+}
+
+template <bool GROUPED, bool BF16, bool DW>
 __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kGemmStageBytes];   // [stage][A, B]
   __shared__ std::conditional_t<GROUPED, GroupTable, NoTable> table;
-  // XCD-aware order: XCD x takes items [x * per_xcd, ...); items run over
-  // blocks of kGemmXcdBlock x kGemmXcdBlock tiles, row-major inside a block.
+
+  // tile order: XCD x owns ordered tiles [x * per_xcd, (x + 1) * per_xcd)
+  const uint32_t tiles = a.tiles_m * a.tiles_n;
   const uint32_t id = (blockIdx.x % 8) * a.per_xcd + blockIdx.x / 8;
-  if (id >= a.items)
+  if (id >= tiles)
     return;  // uniform, before any barrier
-  const uint32_t bn = (a.tiles_n + kGemmXcdBlock - 1) / kGemmXcdBlock;
-  const uint32_t blk = id / (kGemmXcdBlock * kGemmXcdBlock), in = id % (kGemmXcdBlock * kGemmXcdBlock);
-  const uint32_t bm_i = blk / bn, bn_i = blk % bn;
-  const uint32_t rows_here = min((uint32_t)kGemmXcdBlock, a.tiles_m - bm_i * kGemmXcdBlock);
-  const uint32_t cols_here = min((uint32_t)kGemmXcdBlock, a.tiles_n - bn_i * kGemmXcdBlock);
-  if (in >= rows_here * cols_here)
-    return;
-  const uint32_t tm = bm_i * kGemmXcdBlock + in / cols_here;
-  const uint32_t tn = bn_i * kGemmXcdBlock + in % cols_here;
+  const uint32_t band = id / (kGemmBand * a.tiles_n);
+  const uint32_t band_rows = min((uint32_t)kGemmBand, a.tiles_m - band * kGemmBand);
+  const uint32_t within = id - band * kGemmBand * a.tiles_n;
+  const uint32_t tm = band * kGemmBand + within % band_rows;
+  const uint32_t tn = within / band_rows;
 
   const int64_t k = a.k;
+  const int64_t kb = k / 32;
   const uint8_t* qb = a.qb;
   const uint8_t* sb = a.sb;
   int64_t row0, rows_valid;
@@ -141,7 +139,7 @@ __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
     row0 = table.lo[g] + (pos - table.start[g]);
     rows_valid = min((int64_t)kGemmTile, (int64_t)table.hi[g] - row0);
     qb += (int64_t)g * a.n * k;
-    sb += (int64_t)g * a.n * (k / 32);
+    sb += (int64_t)g * a.n * kb;
   } else {
     row0 = (int64_t)tm * kGemmTile;
     rows_valid = min((int64_t)kGemmTile, a.m - row0);
@@ -149,59 +147,136 @@ __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
   const int64_t col0 = (int64_t)tn * kGemmTile;
   const int64_t cols_valid = min((int64_t)kGemmTile, a.n - col0);
 
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
+  // ranges over the tile's rows of A and of B (rows past them read zero)
+  const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(a.qa + row0 * k, (uint32_t)(rows_valid * k));
+  const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(qb + col0 * k, (uint32_t)(cols_valid * k));
+  const __amdgpu_buffer_rsrc_t rsa = buffer_rsrc(a.sa + row0 * kb, (uint32_t)(rows_valid * kb));
+  const __amdgpu_buffer_rsrc_t rsb = buffer_rsrc(sb + col0 * kb, (uint32_t)(cols_valid * kb));
+
+  const int t = threadIdx.x;
+  // loader role: rows t / 8 + 32 u, chunk t % 8 of each stage
+  const int lrow = t / 8, lchunk = t % 8;
+  const int g_off = lrow * (int)k + 16 * lchunk;          // + 32 u k (u < 8: < 2^31 for k <= 2^23)
+  const int w_off = lds_chunk(lrow, lchunk);               // + 4096 u
+  // MFMA role
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int lane = t & 63;
   const int wm = wave >> 1, wn = wave & 1;
   const int r = lane & 31, h = lane >> 5;
-  // the wave's 64 rows of A and 64 rows of B (columns of C)
-  const int64_t ar0 = row0 + wm * 64, br0 = col0 + wn * 64;
-  const int64_t a_rows = max((int64_t)0, min((int64_t)64, rows_valid - wm * 64));
-  const int64_t b_rows = max((int64_t)0, min((int64_t)64, cols_valid - wn * 64));
-  const int64_t kb = k / 32;
-  const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(a.qa + (a_rows ? ar0 : 0) * k, (uint32_t)(a_rows * k));
-  const __amdgpu_buffer_rsrc_t rsa = buffer_rsrc(a.sa + (a_rows ? ar0 : 0) * kb, (uint32_t)(a_rows * kb));
-  const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(qb + (b_rows ? br0 : 0) * k, (uint32_t)(b_rows * k));
-  const __amdgpu_buffer_rsrc_t rsb = buffer_rsrc(sb + (b_rows ? br0 : 0) * kb, (uint32_t)(b_rows * kb));
-  int a_off[2], b_off[2], sa_off[2], sb_off[2];
+  const int fr = (r & 7) ^ ((r >> 3) & 1);
+  const int a_base = (wm * 128 + r) * kGemmTK, b_base = (wn * 128 + r) * kGemmTK;
+  int sa_off[kGemmWaveBlocks], sb_off[kGemmWaveBlocks];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    a_off[i] = (int)((32 * i + r) * k) + 16 * h;
-    b_off[i] = a_off[i];
-    sa_off[i] = (int)((32 * i + r) * kb) + h;
-    sb_off[i] = sa_off[i];
+  for (int i = 0; i < kGemmWaveBlocks; ++i) {
+    sa_off[i] = (wm * 128 + 32 * i + r) * (int)kb;
+    sb_off[i] = (wn * 128 + 32 * i + r) * (int)kb;
   }
 
-  v16f acc[2][2];
+  v16f acc[kGemmWaveBlocks][kGemmWaveBlocks];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < kGemmWaveBlocks; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < kGemmWaveBlocks; ++j)
       acc[i][j] = (v16f){};
-  const int steps = (int)((k + kGemmStep - 1) / kGemmStep);
-  Operands cur, nxt;
-  load_step(cur, ra, rsa, rb, rsb, a_off, b_off, sa_off, sb_off, 0, 32 < k, h == 0 || 32 < k);
-  for (int s = 0; s < steps; ++s) {
-    if (s + 1 < steps) {
-      const int k1 = (s + 1) * kGemmStep;
-      load_step(nxt, ra, rsa, rb, rsb, a_off, b_off, sa_off, sb_off, k1, k1 + 32 < k, h == 0 || k1 + 32 < k);
+
+  const int stages = (int)((k + kGemmTK - 1) / kGemmTK);
+  u32x4 ga[kGemmLoads], gb[kGemmLoads];
+  uint32_t sca[kGemmWaveBlocks], scb[kGemmWaveBlocks], nsa[kGemmWaveBlocks], nsb[kGemmWaveBlocks];
+
+  auto load_stage = [&](int kt) {
+    const bool ok = kt + 16 * lchunk < k;   // chunks past K stay zero
+#pragma unroll
+    for (int u = 0; u < kGemmLoads; ++u) {
+      ga[u] = (u32x4){0, 0, 0, 0};
+      gb[u] = (u32x4){0, 0, 0, 0};
+      if (ok) {
+        ga[u] = __builtin_amdgcn_raw_buffer_load_b128(ra, g_off + u * kGemmLoadRows * (int)k, kt, 0);
+        gb[u] = __builtin_amdgcn_raw_buffer_load_b128(rb, g_off + u * kGemmLoadRows * (int)k, kt, 0);
+      }
     }
-    mma_step(acc, cur);
-    cur = nxt;
+  };
+  auto load_scales = [&](int kt, uint32_t (&s_a)[kGemmWaveBlocks], uint32_t (&s_b)[kGemmWaveBlocks]) {
+#pragma unroll
+    for (int i = 0; i < kGemmWaveBlocks; ++i) {
+      s_a[i] = stage_scales<DW>(rsa, sa_off[i], kt, kb);
+      s_b[i] = stage_scales<DW>(rsb, sb_off[i], kt, kb);
+    }
+  };
+  auto write_stage = [&](int st) {
+    uint8_t* la = lds[st][0] + w_off;
+    uint8_t* lb = lds[st][1] + w_off;
+#pragma unroll
+    for (int u = 0; u < kGemmLoads; ++u) {
+      *reinterpret_cast<u32x4*>(la + u * kGemmLoadRows * kGemmTK) = ga[u];
+      *reinterpret_cast<u32x4*>(lb + u * kGemmLoadRows * kGemmTK) = gb[u];
+    }
+  };
+  // operand of slab i for MFMA step s: chunks 4 s + h and 4 s + 2 + h
+  auto read_slab = [&](const uint8_t* base, int i, int s) {
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(base + i * 32 * kGemmTK + 16 * ((4 * s + h) ^ fr));
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(base + i * 32 * kGemmTK + 16 * ((4 * s + 2 + h) ^ fr));
+    return (v8i){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  };
+  auto compute_stage = [&](int st) {
+    const uint8_t* la = lds[st][0] + a_base;
+    const uint8_t* lb = lds[st][1] + b_base;
+#pragma unroll
+    for (int s = 0; s < kGemmTK / 64; ++s) {
+      v8i fa[kGemmWaveBlocks], fb[kGemmWaveBlocks];
+      int xa[kGemmWaveBlocks], xb[kGemmWaveBlocks];
+#pragma unroll
+      for (int i = 0; i < kGemmWaveBlocks; ++i) {
+        fa[i] = read_slab(la, i, s);
+        fb[i] = read_slab(lb, i, s);
+        // this lane's block of the step is stage block 2 s + h
+        xa[i] = (int)((sca[i] >> (16 * s + 8 * h)) & 0xFFu);
+        xb[i] = (int)((scb[i] >> (16 * s + 8 * h)) & 0xFFu);
+      }
+#pragma unroll
+      for (int i = 0; i < kGemmWaveBlocks; ++i)
+#pragma unroll
+        for (int j = 0; j < kGemmWaveBlocks; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, 0, xa[i], 0,
+                                                                      xb[j]);
+    }
+  };
+
+  if (stages > 0) {
+    load_stage(0);
+    load_scales(0, sca, scb);
+    write_stage(0);
+    lds_barrier();
+  }
+  for (int st = 0; st < stages; ++st) {
+    const bool more = st + 1 < stages;
+    if (more) {
+      load_stage((st + 1) * kGemmTK);
+      load_scales((st + 1) * kGemmTK, nsa, nsb);
+    }
+    compute_stage(st & 1);
+    if (more)
+      write_stage((st + 1) & 1);
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < kGemmWaveBlocks; ++i) {
+      sca[i] = nsa[i];
+      scb[i] = nsb[i];
+    }
   }
 
   // epilogue: register v of lane l is row 8 (v / 4) + 4 h + v % 4, column r
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < kGemmWaveBlocks; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t col = br0 + 32 * j + r;
-      if (col - col0 >= cols_valid)
+    for (int j = 0; j < kGemmWaveBlocks; ++j) {
+      const int64_t lc = wn * 128 + 32 * j + r;   // column within the tile
+      if (lc >= cols_valid)
         continue;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int64_t lr = wm * 64 + 32 * i + 8 * (v / 4) + 4 * h + (v % 4);   // row within the tile
+        const int64_t lr = wm * 128 + 32 * i + 8 * (v / 4) + 4 * h + (v % 4);   // row within the tile
         if (lr < rows_valid) {
-          const int64_t idx = (row0 + lr) * a.n + col;
+          const int64_t idx = (row0 + lr) * a.n + col0 + lc;
           if (BF16)
             static_cast<uint16_t*>(a.c)[idx] = to_bf16(acc[i][j][v]);
           else
@@ -230,11 +305,7 @@ static GemmArgs gemm_args(const uint8_t* qa, const uint8_t* sa, const uint8_t* q
   const int64_t tn = (n + kGemmTile - 1) / kGemmTile;
   a.tiles_m = (uint32_t)tm;
   a.tiles_n = (uint32_t)tn;
-  // items: whole kGemmXcdBlock^2 blocks, so that the block arithmetic holds
-  const int64_t bm = (tm + kGemmXcdBlock - 1) / kGemmXcdBlock, bn = (tn + kGemmXcdBlock - 1) / kGemmXcdBlock;
-  const int64_t items = bm * bn * kGemmXcdBlock * kGemmXcdBlock;
-  a.items = (uint32_t)items;
-  const int64_t per = (items + 7) / 8;
+  const int64_t per = (tm * tn + 7) / 8;
   a.per_xcd = (uint32_t)per;
   *blocks = per * 8;
   return a;
@@ -246,23 +317,32 @@ int64_t gemm_grid_blocks(int64_t m, int64_t n, bool grouped, int32_t groups) {
   return blocks;
 }
 
+template <bool DW>
+static void launch_gemm_dw(const GemmArgs& a, bool grouped, bool bf16, dim3 grid, hipStream_t stream) {
+  const dim3 block(kGemmThreads);
+  if (grouped) {
+    if (bf16)
+      hipLaunchKernelGGL((mx_gemm_kernel<true, true, DW>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((mx_gemm_kernel<true, false, DW>), grid, block, 0, stream, a);
+  } else {
+    if (bf16)
+      hipLaunchKernelGGL((mx_gemm_kernel<false, true, DW>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((mx_gemm_kernel<false, false, DW>), grid, block, 0, stream, a);
+  }
+}
+
 hipError_t launch_mx_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, const uint8_t* sb, int64_t m,
                           int64_t n, int64_t k, void* c, bool bf16, const int32_t* ends, int32_t groups,
                           hipStream_t stream) {
   int64_t blocks;
   const GemmArgs a = gemm_args(qa, sa, qb, sb, m, n, k, c, ends != nullptr, ends, groups, &blocks);
-  const dim3 grid((unsigned)blocks), block(kGemmThreads);
-  if (ends != nullptr) {
-    if (bf16)
-      hipLaunchKernelGGL((mx_gemm_kernel<true, true>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((mx_gemm_kernel<true, false>), grid, block, 0, stream, a);
-  } else {
-    if (bf16)
-      hipLaunchKernelGGL((mx_gemm_kernel<false, true>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((mx_gemm_kernel<false, false>), grid, block, 0, stream, a);
-  }
+  const dim3 grid((unsigned)blocks);
+  if (k % kGemmTK == 0)
+    launch_gemm_dw<true>(a, ends != nullptr, bf16, grid, stream);
+  else
+    launch_gemm_dw<false>(a, ends != nullptr, bf16, grid, stream);
   return hipGetLastError();
 }
 
