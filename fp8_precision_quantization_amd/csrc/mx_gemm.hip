@@ -49,6 +49,8 @@
 #include "mxcast.h"
 #include "mx_launch.h"
 
+#include <type_traits>
+
 namespace mx {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -92,11 +94,11 @@ __device__ __forceinline__ uint16_t to_bf16(float f) {
 
 // The four block scales (bytes) of the stage at K offset kt for the row
 // whose scales start at row_off (bytes) in rs.  DW: the row's scales are
-// dword-aligned (K % 128 == 0) and the stage lies inside K.
+// dword-aligned (K % 128 == 0).
 template <bool DW>
 __device__ __forceinline__ uint32_t stage_scales(__amdgpu_buffer_rsrc_t rs, int row_off, int kt, int64_t kb) {
-  if (DW)
-    return __builtin_amdgcn_raw_buffer_load_b32(rs, row_off, kt / 32, 0);
+  if (DW)   // a stage past K reads zero (its data is zero too)
+    return __builtin_amdgcn_raw_buffer_load_b32(rs, kt / 32 < kb ? row_off : (int)0x80000000, kt / 32, 0);
   uint32_t w = 0;
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
@@ -154,13 +156,17 @@ __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
   const __amdgpu_buffer_rsrc_t rsb = buffer_rsrc(sb + col0 * kb, (uint32_t)(cols_valid * kb));
 
   const int t = threadIdx.x;
-  // loader role: rows t / 8 + 32 u, chunk t % 8 of each stage
-  const int lrow = t / 8, lchunk = t % 8;
-  const int g_off = lrow * (int)k + 16 * lchunk;          // + 32 u k (u < 8: < 2^31 for k <= 2^23)
-  const int w_off = lds_chunk(lrow, lchunk);               // + 4096 u
-  // MFMA role
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int lane = t & 63;
+  // Loader role: load instruction u of wave w fills stage rows 32 u + 8 w ..
+  // + 7 (1 KiB of LDS, 16 bytes per lane in lane order); lane l writes row
+  // position l % 8 of row 32 u + 8 w + l / 8, which holds chunk
+  // (l % 8) ^ f(row).  f(row) depends on row % 16 only, so the chunk and the
+  // row's offset are the same for every u but for 32 u rows.
+  const int lrow = 8 * wave + lane / 8;
+  const int lchunk = (lane % 8) ^ ((lrow & 7) ^ ((lrow >> 3) & 1));
+  const int g_off = lrow * (int)k + 16 * lchunk;          // + 32 u k (< 2^31 for k <= 2^23)
+  // MFMA role
   const int wm = wave >> 1, wn = wave & 1;
   const int r = lane & 31, h = lane >> 5;
   const int fr = (r & 7) ^ ((r >> 3) & 1);
@@ -180,19 +186,21 @@ __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
       acc[i][j] = (v16f){};
 
   const int stages = (int)((k + kGemmTK - 1) / kGemmTK);
-  u32x4 ga[kGemmLoads], gb[kGemmLoads];
-  uint32_t sca[kGemmWaveBlocks], scb[kGemmWaveBlocks], nsa[kGemmWaveBlocks], nsb[kGemmWaveBlocks];
+  uint32_t s0a[kGemmWaveBlocks], s0b[kGemmWaveBlocks], s1a[kGemmWaveBlocks], s1b[kGemmWaveBlocks];
 
-  auto load_stage = [&](int kt) {
-    const bool ok = kt + 16 * lchunk < k;   // chunks past K stay zero
+  // The stage at K offset kt, from memory straight into LDS stage st.
+  // Chunks past K (all of them when kt >= K) get an offset past the
+  // buffer's range and load zero.
+  auto load_stage = [&](auto st_c, int kt) {
+    constexpr int st = decltype(st_c)::value;
+    const int off = kt + (DW ? 0 : 16 * lchunk) < k ? g_off : (int)0x80000000;
 #pragma unroll
     for (int u = 0; u < kGemmLoads; ++u) {
-      ga[u] = (u32x4){0, 0, 0, 0};
-      gb[u] = (u32x4){0, 0, 0, 0};
-      if (ok) {
-        ga[u] = __builtin_amdgcn_raw_buffer_load_b128(ra, g_off + u * kGemmLoadRows * (int)k, kt, 0);
-        gb[u] = __builtin_amdgcn_raw_buffer_load_b128(rb, g_off + u * kGemmLoadRows * (int)k, kt, 0);
-      }
+      const int row = u * kGemmLoadRows + 8 * wave;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)(lds[st][0] + row * kGemmTK),
+                                               16, off + u * kGemmLoadRows * (int)k, kt, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (__attribute__((address_space(3))) void*)(lds[st][1] + row * kGemmTK),
+                                               16, off + u * kGemmLoadRows * (int)k, kt, 0, 0);
     }
   };
   auto load_scales = [&](int kt, uint32_t (&s_a)[kGemmWaveBlocks], uint32_t (&s_b)[kGemmWaveBlocks]) {
@@ -202,14 +210,10 @@ __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
       s_b[i] = stage_scales<DW>(rsb, sb_off[i], kt, kb);
     }
   };
-  auto write_stage = [&](int st) {
-    uint8_t* la = lds[st][0] + w_off;
-    uint8_t* lb = lds[st][1] + w_off;
-#pragma unroll
-    for (int u = 0; u < kGemmLoads; ++u) {
-      *reinterpret_cast<u32x4*>(la + u * kGemmLoadRows * kGemmTK) = ga[u];
-      *reinterpret_cast<u32x4*>(lb + u * kGemmLoadRows * kGemmTK) = gb[u];
-    }
+  // every wave's loads into LDS done, then visible to the workgroup
+  auto stage_barrier = [&]() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    lds_barrier();
   };
   // operand of slab i for MFMA step s: chunks 4 s + h and 4 s + 2 + h
   auto read_slab = [&](const uint8_t* base, int i, int s) {
@@ -217,51 +221,62 @@ __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
     const u32x4 hi = *reinterpret_cast<const u32x4*>(base + i * 32 * kGemmTK + 16 * ((4 * s + 2 + h) ^ fr));
     return (v8i){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
   };
-  auto compute_stage = [&](int st) {
-    const uint8_t* la = lds[st][0] + a_base;
-    const uint8_t* lb = lds[st][1] + b_base;
-#pragma unroll
-    for (int s = 0; s < kGemmTK / 64; ++s) {
-      v8i fa[kGemmWaveBlocks], fb[kGemmWaveBlocks];
-      int xa[kGemmWaveBlocks], xb[kGemmWaveBlocks];
-#pragma unroll
-      for (int i = 0; i < kGemmWaveBlocks; ++i) {
-        fa[i] = read_slab(la, i, s);
-        fb[i] = read_slab(lb, i, s);
-        // this lane's block of the step is stage block 2 s + h
-        xa[i] = (int)((sca[i] >> (16 * s + 8 * h)) & 0xFFu);
-        xb[i] = (int)((scb[i] >> (16 * s + 8 * h)) & 0xFFu);
-      }
-#pragma unroll
-      for (int i = 0; i < kGemmWaveBlocks; ++i)
-#pragma unroll
-        for (int j = 0; j < kGemmWaveBlocks; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, 0, xa[i], 0,
-                                                                      xb[j]);
-    }
-  };
-
-  if (stages > 0) {
-    load_stage(0);
-    load_scales(0, sca, scb);
-    write_stage(0);
-    lds_barrier();
-  }
-  for (int st = 0; st < stages; ++st) {
-    const bool more = st + 1 < stages;
-    if (more) {
-      load_stage((st + 1) * kGemmTK);
-      load_scales((st + 1) * kGemmTK, nsa, nsb);
-    }
-    compute_stage(st & 1);
-    if (more)
-      write_stage((st + 1) & 1);
-    lds_barrier();
+  auto mma = [&](int s, const v8i (&fa)[kGemmWaveBlocks], const v8i (&fb)[kGemmWaveBlocks],
+                 const uint32_t (&sc_a)[kGemmWaveBlocks], const uint32_t (&sc_b)[kGemmWaveBlocks]) {
+    // this lane's block of step s is stage block 2 s + h
+    int xa[kGemmWaveBlocks], xb[kGemmWaveBlocks];
 #pragma unroll
     for (int i = 0; i < kGemmWaveBlocks; ++i) {
-      sca[i] = nsa[i];
-      scb[i] = nsb[i];
+      xa[i] = (int)((sc_a[i] >> (16 * s + 8 * h)) & 0xFFu);
+      xb[i] = (int)((sc_b[i] >> (16 * s + 8 * h)) & 0xFFu);
     }
+#pragma unroll
+    for (int i = 0; i < kGemmWaveBlocks; ++i)
+#pragma unroll
+      for (int j = 0; j < kGemmWaveBlocks; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, 0, xa[i], 0,
+                                                                    xb[j]);
+  };
+  // One stage from LDS stage st with scales cur; meanwhile the next stage
+  // (K offset kn) is loaded into the other LDS stage and its scales into
+  // nxt; all synchronised at the end.
+  auto stage = [&](auto st_c, int kn, const uint32_t (&cur_a)[kGemmWaveBlocks],
+                   const uint32_t (&cur_b)[kGemmWaveBlocks], uint32_t (&nxt_a)[kGemmWaveBlocks],
+                   uint32_t (&nxt_b)[kGemmWaveBlocks]) {
+    constexpr int st = decltype(st_c)::value;
+    const uint8_t* la = lds[st][0] + a_base;
+    const uint8_t* lb = lds[st][1] + b_base;
+    v8i fa0[kGemmWaveBlocks], fb0[kGemmWaveBlocks], fa1[kGemmWaveBlocks], fb1[kGemmWaveBlocks];
+#pragma unroll
+    for (int i = 0; i < kGemmWaveBlocks; ++i) {
+      fa0[i] = read_slab(la, i, 0);
+      fb0[i] = read_slab(lb, i, 0);
+    }
+    load_stage(std::integral_constant<int, st ^ 1>(), kn);
+    load_scales(kn, nxt_a, nxt_b);
+#pragma unroll
+    for (int i = 0; i < kGemmWaveBlocks; ++i) {
+      fa1[i] = read_slab(la, i, 1);
+      fb1[i] = read_slab(lb, i, 1);
+    }
+    mma(0, fa0, fb0, cur_a, cur_b);
+    mma(1, fa1, fb1, cur_a, cur_b);
+    stage_barrier();
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+
+  // Stages alternate between LDS halves 0 and 1 and scale registers s0 /
+  // s1, two per trip; an odd count ends with one stage past K, whose data
+  // and scales load as zero and add nothing.
+  if (stages > 0) {
+    load_stage(S0(), 0);
+    load_scales(0, s0a, s0b);
+    stage_barrier();
+  }
+  for (int st = 0; st < stages; st += 2) {
+    stage(S0(), (st + 1) * kGemmTK, s0a, s0b, s1a, s1b);
+    stage(S1(), (st + 2) * kGemmTK, s1a, s1b, s0a, s0b);
   }
 
   // epilogue: register v of lane l is row 8 (v / 4) + 4 h + v % 4, column r
