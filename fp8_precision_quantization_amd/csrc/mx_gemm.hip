@@ -210,16 +210,19 @@ __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
       s_b[i] = stage_scales<DW>(rsb, sb_off[i], kt, kb);
     }
   };
-  // every wave's loads into LDS done, then visible to the workgroup
-  auto stage_barrier = [&]() {
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-    lds_barrier();
-  };
   // operand of slab i for MFMA step s: chunks 4 s + h and 4 s + 2 + h
   auto read_slab = [&](const uint8_t* base, int i, int s) {
     const u32x4 lo = *reinterpret_cast<const u32x4*>(base + i * 32 * kGemmTK + 16 * ((4 * s + h) ^ fr));
     const u32x4 hi = *reinterpret_cast<const u32x4*>(base + i * 32 * kGemmTK + 16 * ((4 * s + 2 + h) ^ fr));
     return (v8i){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  };
+  auto read_step = [&](auto st_c, int s, v8i (&fa)[kGemmWaveBlocks], v8i (&fb)[kGemmWaveBlocks]) {
+    constexpr int st = decltype(st_c)::value;
+#pragma unroll
+    for (int i = 0; i < kGemmWaveBlocks; ++i) {
+      fa[i] = read_slab(lds[st][0] + a_base, i, s);
+      fb[i] = read_slab(lds[st][1] + b_base, i, s);
+    }
   };
   auto mma = [&](int s, const v8i (&fa)[kGemmWaveBlocks], const v8i (&fb)[kGemmWaveBlocks],
                  const uint32_t (&sc_a)[kGemmWaveBlocks], const uint32_t (&sc_b)[kGemmWaveBlocks]) {
@@ -237,31 +240,48 @@ __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, 0, xa[i], 0,
                                                                     xb[j]);
   };
-  // One stage from LDS stage st with scales cur; meanwhile the next stage
-  // (K offset kn) is loaded into the other LDS stage and its scales into
-  // nxt; all synchronised at the end.
-  auto stage = [&](auto st_c, int kn, const uint32_t (&cur_a)[kGemmWaveBlocks],
-                   const uint32_t (&cur_b)[kGemmWaveBlocks], uint32_t (&nxt_a)[kGemmWaveBlocks],
-                   uint32_t (&nxt_b)[kGemmWaveBlocks]) {
+  // one LDS read after each MFMA, so that the reads of the next step's
+  // operands trickle in behind the MFMAs
+  auto interleave = [&]() {
+#pragma unroll
+    for (int q = 0; q < 2 * kGemmWaveBlocks; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // LDS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kGemmWaveBlocks * kGemmWaveBlocks - 2 * kGemmWaveBlocks, 0);
+  };
+  // Stage t (LDS half st = t % 2, K offset kt), entered with its first
+  // step's operands f0 read (or in flight) and its scales in cur:
+  //   - the scales of stage t + 1 are loaded into nxt;
+  //   - the second step's operands are read while the first step multiplies;
+  //   - once this wave's loads of stage t + 1 have landed and every wave is
+  //     past its reads of half st (barrier), stage t + 2 is loaded into
+  //     half st and the first-step operands of stage t + 1 are read from
+  //     the other half while the second step multiplies.
+  // A stage's loads thus have about a stage of MFMA time to arrive, and no
+  // barrier stands between the last MFMA of a stage and the first of the
+  // next.  Stages past K load zero.
+  auto stage = [&](auto st_c, int kt, v8i (&f0a)[kGemmWaveBlocks], v8i (&f0b)[kGemmWaveBlocks],
+                   const uint32_t (&cur_a)[kGemmWaveBlocks], const uint32_t (&cur_b)[kGemmWaveBlocks],
+                   uint32_t (&nxt_a)[kGemmWaveBlocks], uint32_t (&nxt_b)[kGemmWaveBlocks]) {
     constexpr int st = decltype(st_c)::value;
-    const uint8_t* la = lds[st][0] + a_base;
-    const uint8_t* lb = lds[st][1] + b_base;
-    v8i fa0[kGemmWaveBlocks], fb0[kGemmWaveBlocks], fa1[kGemmWaveBlocks], fb1[kGemmWaveBlocks];
-#pragma unroll
-    for (int i = 0; i < kGemmWaveBlocks; ++i) {
-      fa0[i] = read_slab(la, i, 0);
-      fb0[i] = read_slab(lb, i, 0);
-    }
-    load_stage(std::integral_constant<int, st ^ 1>(), kn);
-    load_scales(kn, nxt_a, nxt_b);
-#pragma unroll
-    for (int i = 0; i < kGemmWaveBlocks; ++i) {
-      fa1[i] = read_slab(la, i, 1);
-      fb1[i] = read_slab(lb, i, 1);
-    }
-    mma(0, fa0, fb0, cur_a, cur_b);
-    mma(1, fa1, fb1, cur_a, cur_b);
-    stage_barrier();
+    // (sched_barrier: the compiler keeps these phases in this order)
+    load_scales(kt + kGemmTK, nxt_a, nxt_b);
+    __builtin_amdgcn_sched_barrier(0);
+    v8i f1a[kGemmWaveBlocks], f1b[kGemmWaveBlocks];
+    read_step(st_c, 1, f1a, f1b);
+    mma(0, f0a, f0b, cur_a, cur_b);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    // all but the scale loads just issued: the loads of stage t + 1 (vmcnt)
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kGemmWaveBlocks * (DW ? 1 : 4)));
+    lds_barrier();
+    load_stage(st_c, kt + 2 * kGemmTK);
+    __builtin_amdgcn_sched_barrier(0);
+    read_step(std::integral_constant<int, st ^ 1>(), 0, f0a, f0b);
+    mma(1, f1a, f1b, cur_a, cur_b);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
   };
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
@@ -271,12 +291,19 @@ __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
   // and scales load as zero and add nothing.
   if (stages > 0) {
     load_stage(S0(), 0);
+    load_stage(S1(), kGemmTK);
     load_scales(0, s0a, s0b);
-    stage_barrier();
-  }
-  for (int st = 0; st < stages; st += 2) {
-    stage(S0(), (st + 1) * kGemmTK, s0a, s0b, s1a, s1b);
-    stage(S1(), (st + 2) * kGemmTK, s1a, s1b, s0a, s0b);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    lds_barrier();
+    v8i f0a[kGemmWaveBlocks], f0b[kGemmWaveBlocks];
+    read_step(S0(), 0, f0a, f0b);
+    for (int st = 0; st < stages; st += 2) {
+      stage(S0(), st * kGemmTK, f0a, f0b, s0a, s0b, s1a, s1b);
+      stage(S1(), (st + 1) * kGemmTK, f0a, f0b, s1a, s1b, s0a, s0b);
+    }
+    // the last trip's loads (past K) must land before the workgroup's LDS
+    // is released
+    __builtin_amdgcn_s_waitcnt(0x0F70);
   }
 
   // epilogue: register v of lane l is row 8 (v / 4) + 4 h + v % 4, column r
