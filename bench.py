@@ -468,15 +468,19 @@ def _mx_operands(rows, k, seed, dev):
 def setup_gemm(dev, grouped=False, m=16640, n=8192, k=5120):
     log("generating MX operands")
     qa, sa = _mx_operands(m, k, 101, dev)
+    # scales in the blocked layouts the GEMM reads (arranged before timing)
     if grouped:
         _, ends = workloads.moe_activations()
         g = len(ends)
         ops = [_mx_operands(n, k, 200 + i, dev) for i in range(g)]
         qb = torch.stack([o[0] for o in ops])
-        sb = torch.stack([o[1] for o in ops])
+        sb = mx.mx_scales_to_blocked(torch.stack([o[1] for o in ops]), raw=True)
         offs = torch.from_numpy(ends).to(dev)
+        sa = mx.mx_scales_to_blocked_grouped(sa, offs, 0, raw=True)[0]
     else:
         qb, sb = _mx_operands(n, k, 102, dev)
+        sa = mx.mx_scales_to_blocked(sa, raw=True)
+        sb = mx.mx_scales_to_blocked(sb, raw=True)
     c = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
     timer = Timer(whole_step=True)
     if grouped:
@@ -491,7 +495,7 @@ def setup_gemm(dev, grouped=False, m=16640, n=8192, k=5120):
             call()
 
     flops = 2 * m * n * k
-    config = {"workload": "%s M=%d N=%d K=%d, e4m3 x e4m3 with e8m0 block scales, bf16 out%s"
+    config = {"workload": "%s M=%d N=%d K=%d, e4m3 x e4m3 with e8m0 block scales (blocked layout), bf16 out%s"
                           % ("mx_grouped_gemm_mxfp8" if grouped else "mx_gemm_mxfp8", m, n, k,
                              ", 4 groups along M" if grouped else ""),
               "m": m, "n": n, "k": k, "unit": "TFLOP/s", "bound": "mfma", "peak": MFMA_FP8_PEAK_TFLOPS,

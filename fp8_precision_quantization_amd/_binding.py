@@ -284,11 +284,15 @@ def mx_quantize_fp8_tensorwise(x, out=None, workspace=None, raw: bool = False):
     return q.view(torch.float8_e4m3fn), s.view(torch.bfloat16)
 
 
-def _mx_operand(q, s, rows, k, name):
+def _mx_operand(q, s, rows, k, nbytes, name):
+    """Codes (..., rows, k) and their scales as blocked-layout bytes (any
+    contiguous u8 tensor of nbytes elements)."""
     q = _scale_input(q, name + " codes")
     s = _scale_input(s, name + " scales")
-    if tuple(q.shape[-2:]) != (rows, k) or tuple(s.shape[-2:]) != (rows, k // MX_BLOCK):
-        raise ValueError("%s: codes (%d, %d) and scales (%d, %d) expected" % (name, rows, k, rows, k // MX_BLOCK))
+    if tuple(q.shape[-2:]) != (rows, k):
+        raise ValueError("%s: codes (%d, %d) expected" % (name, rows, k))
+    if s.numel() != nbytes:
+        raise ValueError("%s: %d bytes of blocked scales expected, got %d" % (name, nbytes, s.numel()))
     return q, s
 
 
@@ -303,12 +307,13 @@ def _gemm_out(out, shape, out_dtype, device):
 
 
 def mx_gemm_mxfp8(qa, sa, qb, sb, out_dtype=torch.bfloat16, out=None):
-    """C (M, N) = A @ B^T for MX operands: qa (M, K) e4m3 codes with sa (M,
-    K/32) e8m0 scales, qb (N, K) with sb (N, K/32) -- the dim0 casts' outputs."""
+    """C (M, N) = A @ B^T for MX operands: qa (M, K) e4m3 codes with sa the
+    blocked layout of its (M, K/32) e8m0 scales, qb (N, K) with sb likewise
+    -- the dim0 cast's outputs in its blocked-scale form."""
     m, k = qa.shape
     n = qb.shape[0]
-    qa, sa = _mx_operand(qa, sa, m, k, "A")
-    qb, sb = _mx_operand(qb, sb, n, k, "B")
+    qa, sa = _mx_operand(qa, sa, m, k, mx_blocked_bytes(1, m, k // MX_BLOCK), "A")
+    qb, sb = _mx_operand(qb, sb, n, k, mx_blocked_bytes(1, n, k // MX_BLOCK), "B")
     c = _gemm_out(out, (m, n), out_dtype, qa.device)
     _check(lib().mx_gemm_mxfp8(_ptr(qa), _ptr(sa), _ptr(qb), _ptr(sb), m, n, k, _ptr(c),
                                int(out_dtype == torch.bfloat16), _stream(qa.device)), "mx_gemm_mxfp8")
@@ -316,16 +321,18 @@ def mx_gemm_mxfp8(qa, sa, qb, sb, out_dtype=torch.bfloat16, out=None):
 
 
 def mx_grouped_gemm_mxfp8(qa, sa, qb, sb, group_end_offsets, out_dtype=torch.bfloat16, out=None):
-    """Grouped along M: rows of group g of A times group g's weights, qb (G,
-    N, K) / sb (G, N, K/32); offsets int32 [G] on the device.  Rows past the
-    last end are left as they were in `out`."""
+    """Grouped along M: rows of group g of A times group g's weights.  sa is
+    the M-grouped blocked layout of A's scales (as mx_cast_dim0_dim1_mgrouped
+    writes it), qb (G, N, K) the weights' codes and sb the G blocked layouts
+    of their (N, K/32) scales one after another; offsets int32 [G] on the
+    device.  Rows past the last end are left as they were in `out`."""
     m, k = qa.shape
     g, n, _ = qb.shape
     offs = _offsets(group_end_offsets)
     if offs.numel() != g:
         raise ValueError("one offset per group of B")
-    qa, sa = _mx_operand(qa, sa, m, k, "A")
-    qb, sb = _mx_operand(qb, sb, n, k, "B")
+    qa, sa = _mx_operand(qa, sa, m, k, mx_blocked_grouped_bytes(m, k // MX_BLOCK, g, 0), "A")
+    qb, sb = _mx_operand(qb, sb, n, k, mx_blocked_bytes(g, n, k // MX_BLOCK), "B")
     c = _gemm_out(out, (m, n), out_dtype, qa.device)
     _check(lib().mx_grouped_gemm_mxfp8(_ptr(qa), _ptr(sa), _ptr(qb), _ptr(sb), _ptr(offs), g, m, n, k, _ptr(c),
                                        int(out_dtype == torch.bfloat16), _stream(qa.device)),

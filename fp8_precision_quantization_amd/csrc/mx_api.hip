@@ -34,7 +34,8 @@ mx_status check_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, co
     return MX_OK;
   if (c == nullptr || (k > 0 && (qa == nullptr || sa == nullptr || qb == nullptr || sb == nullptr)))
     return MX_ERR_NULL;
-  if (!aligned(qa, 16) || !aligned(qb, 16) || !aligned(c, c_bf16 ? 2 : 4))
+  if (!aligned(qa, 16) || !aligned(qb, 16) || !aligned(sa, 16) || !aligned(sb, 16) ||
+      !aligned(c, c_bf16 ? 2 : 4))
     return MX_ERR_ALIGN;
   return MX_OK;
 }

@@ -64,7 +64,6 @@ constexpr int kGemmLoadRows = kGemmThreads * 16 / kGemmTK;   // rows per load in
 constexpr int kGemmLoads = kGemmTile / kGemmLoadRows;        // load instructions per operand and stage (8)
 constexpr int kGemmStageBytes = kGemmTile * kGemmTK;         // one operand's stage (32 KiB)
 constexpr int kGemmBand = 8;                   // tile rows per band of the tile order
-constexpr uint32_t kE8m0One = 127;             // e8m0 byte of 2^0
 
 struct GemmArgs {
   const uint8_t *qa, *sa, *qb, *sb;
@@ -72,6 +71,7 @@ struct GemmArgs {
   void* c;
   const int32_t* ends;
   int32_t groups;
+  int64_t sb_bytes;            // bytes of one group's blocked B scales
   uint32_t tiles_m, tiles_n;   // tile grid (tiles_m includes one spare tile per group when grouped)
   uint32_t per_xcd;            // tiles per XCD
 };
@@ -84,6 +84,13 @@ __device__ __forceinline__ int lds_chunk(int row, int c) {
   return row * kGemmTK + 16 * (c ^ ((row & 7) ^ ((row >> 3) & 1)));
 }
 
+__device__ __forceinline__ int32_t wave_sum(int32_t v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1)
+    v += __shfl_xor(v, d);
+  return v;
+}
+
 // binary32 -> bf16 bits, nearest-even; NaN -> 0x7FC0.
 __device__ __forceinline__ uint16_t to_bf16(float f) {
   const uint32_t u = __float_as_uint(f);
@@ -92,27 +99,9 @@ __device__ __forceinline__ uint16_t to_bf16(float f) {
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
-// The four block scales (bytes) of the stage at K offset kt for the row
-// whose scales start at row_off (bytes) in rs.  DW: the row's scales are
-// dword-aligned (K % 128 == 0).
-template <bool DW>
-__device__ __forceinline__ uint32_t stage_scales(__amdgpu_buffer_rsrc_t rs, int row_off, int kt, int64_t kb) {
-  if (DW)   // a stage past K reads zero (its data is zero too)
-    return __builtin_amdgcn_raw_buffer_load_b32(rs, kt / 32 < kb ? row_off : (int)0x80000000, kt / 32, 0);
-  uint32_t w = 0;
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const int blk = kt / 32 + b;
-    const uint32_t v = blk < kb ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs, row_off, blk, 0) : kE8m0One;
-    w |= v << (8 * b);
-  }
-  return w;
-}
-
-template <bool GROUPED, bool BF16, bool DW>
+template <bool GROUPED, bool BF16>
 __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kGemmStageBytes];   // [stage][A, B]
-  __shared__ std::conditional_t<GROUPED, GroupTable, NoTable> table;
 
   // tile order: XCD x owns ordered tiles [x * per_xcd, (x + 1) * per_xcd)
   const uint32_t tiles = a.tiles_m * a.tiles_n;
@@ -129,35 +118,62 @@ __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
   const int64_t kb = k / 32;
   const uint8_t* qb = a.qb;
   const uint8_t* sb = a.sb;
-  int64_t row0, rows_valid;
+  int64_t row0, rows_valid, srow0;
   if constexpr (GROUPED) {
+    // The group table borrows the B half of LDS stage 1 until the first
+    // stages are loaded.  (One LDS object keeps the compiler able to tell
+    // the loads into one stage from the reads of the other.)
+    static_assert(sizeof(GroupTable) <= kGemmStageBytes, "group table fits a stage half");
+    GroupTable& table = *reinterpret_cast<GroupTable*>(lds[1][1]);
     if (threadIdx.x < 64)
       build_group_table(a.ends, a.groups, (int32_t)a.m, kGemmTile, table);
     lds_barrier();
+    // Values read from LDS are per-lane to the compiler; readfirstlane
+    // makes them scalar (they are the same in every lane), so that the
+    // buffer descriptors built from them stay in scalar registers.
     const int32_t pos = (int32_t)tm * kGemmTile;
-    const int g = find_group(table, a.groups, pos);
+    const int g = __builtin_amdgcn_readfirstlane(find_group(table, a.groups, pos));
     if (g < 0)
       return;  // uniform; no barrier follows
-    row0 = table.lo[g] + (pos - table.start[g]);
-    rows_valid = min((int64_t)kGemmTile, (int64_t)table.hi[g] - row0);
+    const int32_t lo = __builtin_amdgcn_readfirstlane(table.lo[g]);
+    const int32_t hi = __builtin_amdgcn_readfirstlane(table.hi[g]);
+    const int32_t r0 = lo + (pos - __builtin_amdgcn_readfirstlane(table.start[g]));
+    row0 = r0;
+    rows_valid = min(kGemmTile, hi - r0);
+    // the tile's first row in A's M-grouped blocked scales: group g starts
+    // there at the sum of the earlier groups' sizes rounded up to 128 rows
+    int32_t part = 0;
+    for (int q = threadIdx.x & 63; q < g; q += 64)
+      part += (table.hi[q] - table.lo[q] + 127) / 128 * 128;
+    srow0 = __builtin_amdgcn_readfirstlane(wave_sum(part)) + (r0 - lo);
+    lds_barrier();   // every wave is done with the table
     qb += (int64_t)g * a.n * k;
-    sb += (int64_t)g * a.n * kb;
+    sb += (int64_t)g * a.sb_bytes;
   } else {
     row0 = (int64_t)tm * kGemmTile;
     rows_valid = min((int64_t)kGemmTile, a.m - row0);
+    srow0 = row0;
   }
   const int64_t col0 = (int64_t)tn * kGemmTile;
   const int64_t cols_valid = min((int64_t)kGemmTile, a.n - col0);
 
-  // ranges over the tile's rows of A and of B (rows past them read zero)
-  const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(a.qa + row0 * k, (uint32_t)(rows_valid * k));
-  const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(qb + col0 * k, (uint32_t)(cols_valid * k));
-  const __amdgpu_buffer_rsrc_t rsa = buffer_rsrc(a.sa + row0 * kb, (uint32_t)(rows_valid * kb));
-  const __amdgpu_buffer_rsrc_t rsb = buffer_rsrc(sb + col0 * kb, (uint32_t)(cols_valid * kb));
-
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int lane = t & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // ranges over the tile's rows of A and of B (rows past them read zero)
+  const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(a.qa + row0 * k, (uint32_t)(rows_valid * k));
+  const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(qb + col0 * k, (uint32_t)(cols_valid * k));
+  // Scales: the wave's 128 rows of A (and of B) are one row of 128 x 4
+  // tiles of the blocked layout, a strip of 512 bytes per stage; a wave
+  // whose rows all lie past the tile's end reads zero scales.
+  const int64_t strip = (kb + 3) / 4 * 512;
+  const bool a_on = rows_valid > wm * 128, b_on = cols_valid > wn * 128;
+  const __amdgpu_buffer_rsrc_t rsa =
+      buffer_rsrc(a.sa + (a_on ? (srow0 + wm * 128) / 128 * strip : 0), a_on ? (uint32_t)strip : 0u);
+  const __amdgpu_buffer_rsrc_t rsb =
+      buffer_rsrc(sb + (b_on ? (col0 + wn * 128) / 128 * strip : 0), b_on ? (uint32_t)strip : 0u);
   // Loader role: load instruction u of wave w fills stage rows 32 u + 8 w ..
   // + 7 (1 KiB of LDS, 16 bytes per lane in lane order); lane l writes row
   // position l % 8 of row 32 u + 8 w + l / 8, which holds chunk
@@ -167,16 +183,9 @@ __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
   const int lchunk = (lane % 8) ^ ((lrow & 7) ^ ((lrow >> 3) & 1));
   const int g_off = lrow * (int)k + 16 * lchunk;          // + 32 u k (< 2^31 for k <= 2^23)
   // MFMA role
-  const int wm = wave >> 1, wn = wave & 1;
   const int r = lane & 31, h = lane >> 5;
   const int fr = (r & 7) ^ ((r >> 3) & 1);
   const int a_base = (wm * 128 + r) * kGemmTK, b_base = (wn * 128 + r) * kGemmTK;
-  int sa_off[kGemmWaveBlocks], sb_off[kGemmWaveBlocks];
-#pragma unroll
-  for (int i = 0; i < kGemmWaveBlocks; ++i) {
-    sa_off[i] = (wm * 128 + 32 * i + r) * (int)kb;
-    sb_off[i] = (wn * 128 + 32 * i + r) * (int)kb;
-  }
 
   v16f acc[kGemmWaveBlocks][kGemmWaveBlocks];
 #pragma unroll
@@ -188,118 +197,134 @@ __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
   const int stages = (int)((k + kGemmTK - 1) / kGemmTK);
   uint32_t s0a[kGemmWaveBlocks], s0b[kGemmWaveBlocks], s1a[kGemmWaveBlocks], s1b[kGemmWaveBlocks];
 
-  // The stage at K offset kt, from memory straight into LDS stage st.
-  // Chunks past K (all of them when kt >= K) get an offset past the
-  // buffer's range and load zero.
-  auto load_stage = [&](auto st_c, int kt) {
+  // Load u (0 .. 15) of a stage: load instruction u / 2 of operand u % 2,
+  // from memory straight into LDS half st.  Chunks past K (all of them when
+  // kt >= K) get an offset past the buffer's range and load zero.
+  auto load_one = [&](auto st_c, int kt, int u) {
     constexpr int st = decltype(st_c)::value;
-    const int off = kt + (DW ? 0 : 16 * lchunk) < k ? g_off : (int)0x80000000;
-#pragma unroll
-    for (int u = 0; u < kGemmLoads; ++u) {
-      const int row = u * kGemmLoadRows + 8 * wave;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)(lds[st][0] + row * kGemmTK),
-                                               16, off + u * kGemmLoadRows * (int)k, kt, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (__attribute__((address_space(3))) void*)(lds[st][1] + row * kGemmTK),
-                                               16, off + u * kGemmLoadRows * (int)k, kt, 0, 0);
-    }
+    const int off = kt + 16 * lchunk < k ? g_off : (int)0x80000000;
+    const int row = (u / 2) * kGemmLoadRows + 8 * wave;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(u % 2 ? rb : ra,
+                                             (__attribute__((address_space(3))) void*)(lds[st][u % 2] + row * kGemmTK),
+                                             16, off + (u / 2) * kGemmLoadRows * (int)k, kt, 0, 0);
   };
+  // The stage's scales: lane r + 32 h reads bytes 16 r .. + 15 of the
+  // stage's 512-byte tile, whose dword i holds the four block scales of row
+  // 32 i + r.  Blocks past K are the layout's zero padding (their data is
+  // zero too); a stage past K reads zero.
   auto load_scales = [&](int kt, uint32_t (&s_a)[kGemmWaveBlocks], uint32_t (&s_b)[kGemmWaveBlocks]) {
+    const u32x4 va = __builtin_amdgcn_raw_buffer_load_b128(rsa, 16 * r, kt / kGemmTK * 512, 0);
+    const u32x4 vb = __builtin_amdgcn_raw_buffer_load_b128(rsb, 16 * r, kt / kGemmTK * 512, 0);
 #pragma unroll
     for (int i = 0; i < kGemmWaveBlocks; ++i) {
-      s_a[i] = stage_scales<DW>(rsa, sa_off[i], kt, kb);
-      s_b[i] = stage_scales<DW>(rsb, sb_off[i], kt, kb);
+      s_a[i] = va[i];
+      s_b[i] = vb[i];
     }
   };
-  // operand of slab i for MFMA step s: chunks 4 s + h and 4 s + 2 + h
-  auto read_slab = [&](const uint8_t* base, int i, int s) {
-    const u32x4 lo = *reinterpret_cast<const u32x4*>(base + i * 32 * kGemmTK + 16 * ((4 * s + h) ^ fr));
-    const u32x4 hi = *reinterpret_cast<const u32x4*>(base + i * 32 * kGemmTK + 16 * ((4 * s + 2 + h) ^ fr));
-    return (v8i){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-  };
-  auto read_step = [&](auto st_c, int s, v8i (&fa)[kGemmWaveBlocks], v8i (&fb)[kGemmWaveBlocks]) {
+  // MFMA operands of one step as 16-byte halves: [slab][0] = chunk 4 s + h
+  // (first 32-block of the step), [slab][1] = chunk 4 s + 2 + h (second).
+  typedef u32x4 Half[kGemmWaveBlocks][2];
+  // Read q (0 .. 15) of a step's operands from LDS half st, in the order
+  // the MFMAs consume them: A slab 0, B slabs 0 .. 3, A slabs 1 .. 3, each
+  // as its two halves.
+  auto read_one = [&](auto st_c, int s, int q, Half& fa, Half& fb) {
     constexpr int st = decltype(st_c)::value;
-#pragma unroll
-    for (int i = 0; i < kGemmWaveBlocks; ++i) {
-      fa[i] = read_slab(lds[st][0] + a_base, i, s);
-      fb[i] = read_slab(lds[st][1] + b_base, i, s);
-    }
+    const int slab = q / 2, half = q % 2;   // 0: A0, 1-4: B0-B3, 5-7: A1-A3
+    const bool is_b = slab >= 1 && slab <= 4;
+    const int i = slab == 0 ? 0 : is_b ? slab - 1 : slab - 4;
+    const uint8_t* base = is_b ? lds[st][1] + b_base : lds[st][0] + a_base;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(base + i * 32 * kGemmTK + 16 * ((4 * s + 2 * half + h) ^ fr));
+    (is_b ? fb : fa)[i][half] = v;
   };
-  auto mma = [&](int s, const v8i (&fa)[kGemmWaveBlocks], const v8i (&fb)[kGemmWaveBlocks],
-                 const uint32_t (&sc_a)[kGemmWaveBlocks], const uint32_t (&sc_b)[kGemmWaveBlocks]) {
-    // this lane's block of step s is stage block 2 s + h
-    int xa[kGemmWaveBlocks], xb[kGemmWaveBlocks];
-#pragma unroll
-    for (int i = 0; i < kGemmWaveBlocks; ++i) {
-      xa[i] = (int)((sc_a[i] >> (16 * s + 8 * h)) & 0xFFu);
-      xb[i] = (int)((sc_b[i] >> (16 * s + 8 * h)) & 0xFFu);
-    }
+  auto mfma = [&](int i, int j, const Half& fa, const Half& fb, int xa, int xb) {
+    const v8i va = (v8i){(int)fa[i][0][0], (int)fa[i][0][1], (int)fa[i][0][2], (int)fa[i][0][3],
+                         (int)fa[i][1][0], (int)fa[i][1][1], (int)fa[i][1][2], (int)fa[i][1][3]};
+    const v8i vb = (v8i){(int)fb[j][0][0], (int)fb[j][0][1], (int)fb[j][0][2], (int)fb[j][0][3],
+                         (int)fb[j][1][0], (int)fb[j][1][1], (int)fb[j][1][2], (int)fb[j][1][3]};
+    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, vb, acc[i][j], 0, 0, 0, xa, 0, xb);
+  };
+  // this lane's scale bytes for step s: stage block 2 s + h
+  auto step_scales = [&](int s, const uint32_t (&sc)[kGemmWaveBlocks], int (&x)[kGemmWaveBlocks]) {
 #pragma unroll
     for (int i = 0; i < kGemmWaveBlocks; ++i)
-#pragma unroll
-      for (int j = 0; j < kGemmWaveBlocks; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, 0, xa[i], 0,
-                                                                    xb[j]);
+      x[i] = (int)((sc[i] >> (16 * s + 8 * h)) & 0xFFu);
   };
-  // one LDS read after each MFMA, so that the reads of the next step's
-  // operands trickle in behind the MFMAs
-  auto interleave = [&]() {
-#pragma unroll
-    for (int q = 0; q < 2 * kGemmWaveBlocks; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // LDS read
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, kGemmWaveBlocks * kGemmWaveBlocks - 2 * kGemmWaveBlocks, 0);
-  };
-  // Stage t (LDS half st = t % 2, K offset kt), entered with its first
-  // step's operands f0 read (or in flight) and its scales in cur:
-  //   - the scales of stage t + 1 are loaded into nxt;
-  //   - the second step's operands are read while the first step multiplies;
-  //   - once this wave's loads of stage t + 1 have landed and every wave is
-  //     past its reads of half st (barrier), stage t + 2 is loaded into
-  //     half st and the first-step operands of stage t + 1 are read from
-  //     the other half while the second step multiplies.
-  // A stage's loads thus have about a stage of MFMA time to arrive, and no
-  // barrier stands between the last MFMA of a stage and the first of the
-  // next.  Stages past K load zero.
-  auto stage = [&](auto st_c, int kt, v8i (&f0a)[kGemmWaveBlocks], v8i (&f0b)[kGemmWaveBlocks],
-                   const uint32_t (&cur_a)[kGemmWaveBlocks], const uint32_t (&cur_b)[kGemmWaveBlocks],
-                   uint32_t (&nxt_a)[kGemmWaveBlocks], uint32_t (&nxt_b)[kGemmWaveBlocks]) {
-    constexpr int st = decltype(st_c)::value;
-    // (sched_barrier: the compiler keeps these phases in this order)
+
+  // Stage t (LDS half st = t % 2, K offset kt) runs in two halves.
+  // First half, entered with the first step's operands f0 read (or in
+  // flight) and the stage's scales in cur: the scales of stage t + 1 are
+  // loaded into nxt, and each MFMA of the first step is followed by one LDS
+  // read of the second step's operands f1; then, once this wave's loads of
+  // stage t + 1 have landed and every wave is past its reads of half st,
+  // a barrier.  Second half: each MFMA of the second step is followed by one
+  // load of stage t + 2 into half st and one LDS read of stage t + 1's
+  // first-step operands from the other half.  A stage's loads thus have
+  // about a stage of MFMA time to arrive, and no barrier stands between the
+  // last MFMA of a stage and the first of the next.  Stages past K load
+  // zero.  sched_barrier keeps the compiler to this instruction order.
+  auto first_half = [&](auto st_c, int kt, const Half& f0a, const Half& f0b,
+                        const uint32_t (&cur_a)[kGemmWaveBlocks], const uint32_t (&cur_b)[kGemmWaveBlocks],
+                        uint32_t (&nxt_a)[kGemmWaveBlocks], uint32_t (&nxt_b)[kGemmWaveBlocks], Half& f1a,
+                        Half& f1b) {
     load_scales(kt + kGemmTK, nxt_a, nxt_b);
+    int xa[kGemmWaveBlocks], xb[kGemmWaveBlocks];
+    step_scales(0, cur_a, xa);
+    step_scales(0, cur_b, xb);
     __builtin_amdgcn_sched_barrier(0);
-    v8i f1a[kGemmWaveBlocks], f1b[kGemmWaveBlocks];
-    read_step(st_c, 1, f1a, f1b);
-    mma(0, f0a, f0b, cur_a, cur_b);
-    interleave();
-    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < kGemmWaveBlocks * kGemmWaveBlocks; ++q) {
+      mfma(q / kGemmWaveBlocks, q % kGemmWaveBlocks, f0a, f0b, xa[q / kGemmWaveBlocks], xb[q % kGemmWaveBlocks]);
+      read_one(st_c, 1, q, f1a, f1b);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // all but the scale loads just issued: the loads of stage t + 1 (vmcnt)
-    __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kGemmWaveBlocks * (DW ? 1 : 4)));
+    __builtin_amdgcn_s_waitcnt(0x0F70 | 2);
     lds_barrier();
-    load_stage(st_c, kt + 2 * kGemmTK);
+  };
+  auto second_half = [&](auto st_c, int kt, const Half& f1a, const Half& f1b,
+                         const uint32_t (&cur_a)[kGemmWaveBlocks], const uint32_t (&cur_b)[kGemmWaveBlocks],
+                         Half& f0a, Half& f0b) {
+    constexpr int st = decltype(st_c)::value;
+    int xa[kGemmWaveBlocks], xb[kGemmWaveBlocks];
+    step_scales(1, cur_a, xa);
+    step_scales(1, cur_b, xb);
     __builtin_amdgcn_sched_barrier(0);
-    read_step(std::integral_constant<int, st ^ 1>(), 0, f0a, f0b);
-    mma(1, f1a, f1b, cur_a, cur_b);
-    interleave();
-    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < kGemmWaveBlocks * kGemmWaveBlocks; ++q) {
+      mfma(q / kGemmWaveBlocks, q % kGemmWaveBlocks, f1a, f1b, xa[q / kGemmWaveBlocks], xb[q % kGemmWaveBlocks]);
+      load_one(st_c, kt + 2 * kGemmTK, q);
+      read_one(std::integral_constant<int, st ^ 1>(), 0, q, f0a, f0b);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
+  static_assert(2 * kGemmLoads == kGemmWaveBlocks * kGemmWaveBlocks, "one load per second-step MFMA");
 
   // Stages alternate between LDS halves 0 and 1 and scale registers s0 /
-  // s1, two per trip; an odd count ends with one stage past K, whose data
-  // and scales load as zero and add nothing.
+  // s1.  The loop runs from a barrier to a barrier (no LDS read in flight
+  // at its head), two stages per trip; it ends with the first half of the
+  // stage after the last (an odd count: of two), past K, whose data and
+  // scales load as zero and add nothing.
   if (stages > 0) {
-    load_stage(S0(), 0);
-    load_stage(S1(), kGemmTK);
+#pragma unroll
+    for (int u = 0; u < 2 * kGemmLoads; ++u) {
+      load_one(S0(), 0, u);
+      load_one(S1(), kGemmTK, u);
+    }
     load_scales(0, s0a, s0b);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     lds_barrier();
-    v8i f0a[kGemmWaveBlocks], f0b[kGemmWaveBlocks];
-    read_step(S0(), 0, f0a, f0b);
+    Half f0a, f0b, f1a, f1b;
+#pragma unroll
+    for (int q = 0; q < 2 * kGemmLoads; ++q)
+      read_one(S0(), 0, q, f0a, f0b);
+    first_half(S0(), 0, f0a, f0b, s0a, s0b, s1a, s1b, f1a, f1b);
     for (int st = 0; st < stages; st += 2) {
-      stage(S0(), st * kGemmTK, f0a, f0b, s0a, s0b, s1a, s1b);
-      stage(S1(), (st + 1) * kGemmTK, f0a, f0b, s1a, s1b, s0a, s0b);
+      second_half(S0(), st * kGemmTK, f1a, f1b, s0a, s0b, f0a, f0b);
+      first_half(S1(), (st + 1) * kGemmTK, f0a, f0b, s1a, s1b, s0a, s0b, f1a, f1b);
+      second_half(S1(), (st + 1) * kGemmTK, f1a, f1b, s1a, s1b, f0a, f0b);
+      first_half(S0(), (st + 2) * kGemmTK, f0a, f0b, s0a, s0b, s1a, s1b, f1a, f1b);
     }
     // the last trip's loads (past K) must land before the workgroup's LDS
     // is released
@@ -342,6 +367,7 @@ static GemmArgs gemm_args(const uint8_t* qa, const uint8_t* sa, const uint8_t* q
   a.c = c;
   a.ends = ends;
   a.groups = groups;
+  a.sb_bytes = (n + 127) / 128 * 128 * ((k / 32 + 3) / 4 * 4);
   // grouped: every group may end with a partial tile -> one spare tile each
   const int64_t tm = (m + kGemmTile - 1) / kGemmTile + (grouped ? groups : 0);
   const int64_t tn = (n + kGemmTile - 1) / kGemmTile;
@@ -359,32 +385,24 @@ int64_t gemm_grid_blocks(int64_t m, int64_t n, bool grouped, int32_t groups) {
   return blocks;
 }
 
-template <bool DW>
-static void launch_gemm_dw(const GemmArgs& a, bool grouped, bool bf16, dim3 grid, hipStream_t stream) {
-  const dim3 block(kGemmThreads);
-  if (grouped) {
-    if (bf16)
-      hipLaunchKernelGGL((mx_gemm_kernel<true, true, DW>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((mx_gemm_kernel<true, false, DW>), grid, block, 0, stream, a);
-  } else {
-    if (bf16)
-      hipLaunchKernelGGL((mx_gemm_kernel<false, true, DW>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((mx_gemm_kernel<false, false, DW>), grid, block, 0, stream, a);
-  }
-}
-
 hipError_t launch_mx_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, const uint8_t* sb, int64_t m,
                           int64_t n, int64_t k, void* c, bool bf16, const int32_t* ends, int32_t groups,
                           hipStream_t stream) {
   int64_t blocks;
-  const GemmArgs a = gemm_args(qa, sa, qb, sb, m, n, k, c, ends != nullptr, ends, groups, &blocks);
-  const dim3 grid((unsigned)blocks);
-  if (k % kGemmTK == 0)
-    launch_gemm_dw<true>(a, ends != nullptr, bf16, grid, stream);
-  else
-    launch_gemm_dw<false>(a, ends != nullptr, bf16, grid, stream);
+  const bool grouped = ends != nullptr;
+  const GemmArgs a = gemm_args(qa, sa, qb, sb, m, n, k, c, grouped, ends, groups, &blocks);
+  const dim3 grid((unsigned)blocks), block(kGemmThreads);
+  if (grouped) {
+    if (bf16)
+      hipLaunchKernelGGL((mx_gemm_kernel<true, true>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((mx_gemm_kernel<true, false>), grid, block, 0, stream, a);
+  } else {
+    if (bf16)
+      hipLaunchKernelGGL((mx_gemm_kernel<false, true>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((mx_gemm_kernel<false, false>), grid, block, 0, stream, a);
+  }
   return hipGetLastError();
 }
 

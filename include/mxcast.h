@@ -284,19 +284,28 @@ MX_API mx_status mx_quantize_fp8_tensorwise(const void* x, int64_t n, uint8_t* q
  * compile support", Perf analysis item 1: MXFP8 grouped GEMMs of the MoE
  * activations against per-group weights), on gfx950's block-scaled MFMA:
  *   C[m][n] = sum over k of A(m, k) * B(n, k), with
- *   A(m, k) = e4m3(qa[m][k]) * 2^(sa[m][k / 32] - 127) and B likewise.
- *   qa, sa   A codes (m, k) and scales (m, k / 32) as mx_cast_dim0_dim1
- *            writes q_row / s_row; qa 16-byte aligned.
- *   qb, sb   B codes (n, k) and scales (n, k / 32), K-major the same way
- *            (the dim0 cast of a (n, k) weight); qb 16-byte aligned.
+ *   A(m, k) = e4m3(qa[m][k]) * 2^(S_A(m, k / 32) - 127) and B likewise.
+ *   qa, sa   A codes (m, k) as mx_cast_dim0_dim1 writes q_row, and A's
+ *            (m, k / 32) scales S_A in the 128 x 4 blocked layout
+ *            (mx_blocked_bytes(1, m, k / 32) bytes, as
+ *            mx_cast_dim0_dim1_blocked writes s_row_blocked or
+ *            mx_scales_to_blocked makes); both 16-byte aligned.
+ *   qb, sb   B codes (n, k), K-major the same way (the dim0 cast of a
+ *            (n, k) weight), and B's (n, k / 32) scales blocked likewise;
+ *            both 16-byte aligned.
  *   c        (m, n) row-major: binary32 (c_bf16 = 0, 4-byte aligned) or bf16
  *            rounded to nearest-even (c_bf16 = 1, 2-byte aligned).
+ * The scale layout is the one the scaled-GEMM consumer on the MXFP8 pages
+ * reads: a 32-row slab's scales for four consecutive blocks of K sit in one
+ * 16-byte run.  Padding of the layout (rows past m or n, blocks past
+ * k / 32) is never used for a written result.
  * The products of each 64-deep K step are summed by the MFMA with less than
  * binary32 precision (measured on MI355X: within 3.4e-4 of the step's
  * largest product); the steps accumulate in binary32.  A NaN code or scale
  * (0xFF) gives NaN where it enters.
- * m, n, k >= 0, k % 32 == 0, k <= 2^24, m, n < 2^31, else MX_ERR_SHAPE; m or
- * n 0 writes nothing; k 0 writes zeros.
+ * m, n, k >= 0, k % 32 == 0, k <= 2^23, m, n < 2^31, else MX_ERR_SHAPE; m or
+ * n 0 writes nothing; k 0 writes zeros.  Misaligned pointers give
+ * MX_ERR_ALIGN.
  */
 MX_API mx_status mx_gemm_mxfp8(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, const uint8_t* sb,
                                int64_t m, int64_t n, int64_t k, void* c, int32_t c_bf16, hipStream_t stream);
@@ -304,10 +313,15 @@ MX_API mx_status mx_gemm_mxfp8(const uint8_t* qa, const uint8_t* sa, const uint8
 /*
  * The same GEMM grouped along M: rows [end_{g-1}, end_g) of A (cumulative
  * END offsets on the device, clamped as by mx_scales_to_blocked_grouped)
- * are multiplied by group g's weights, qb / sb holding num_groups
- * consecutive (n, k) / (n, k / 32) matrices.  Rows past the last end are
- * not written.  1 <= num_groups <= MX_MAX_GROUPS (else MX_ERR_GROUPS), m +
- * 128 * num_groups < 2^31; other arguments as for mx_gemm_mxfp8.
+ * are multiplied by group g's weights.  sa holds A's scales in the
+ * M-grouped blocked layout (mx_blocked_grouped_bytes(m, k / 32,
+ * num_groups, 0) bytes, as mx_cast_dim0_dim1_mgrouped writes
+ * s_row_grouped or mx_scales_to_blocked_grouped makes with group_axis 0);
+ * qb holds num_groups consecutive (n, k) code matrices and sb their
+ * num_groups blocked (n, k / 32) scale layouts one after another
+ * (mx_blocked_bytes(num_groups, n, k / 32) bytes).  Rows past the last end
+ * are not written.  1 <= num_groups <= MX_MAX_GROUPS (else MX_ERR_GROUPS),
+ * m + 256 * num_groups < 2^31; other arguments as for mx_gemm_mxfp8.
  */
 MX_API mx_status mx_grouped_gemm_mxfp8(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb,
                                        const uint8_t* sb, const int32_t* group_end_offsets,

@@ -1,6 +1,9 @@
 """GPU parity of the MX-scaled GEMM (dense and grouped along M) with the
 oracle's fp64 definition.  Operands are MX casts made by the ORACLE from
-seeded bf16 data (or seeded random codes and scales), uploaded as they are.
+seeded bf16 data (or seeded random codes and scales); the scales go to the
+GEMM in the blocked layouts, rearranged by the oracle's layout functions.
+The pipeline tests instead feed the GEMM what the library's own casts write
+and compare with the oracle's cast followed by the oracle's GEMM.
 
 Tolerance, from the arithmetic: the block-scaled MFMA sums the 64 products
 of a K step with less than binary32 precision -- an in-bounds probe on
@@ -14,7 +17,7 @@ import torch
 
 import fp8_precision_quantization_amd as mx
 from fp8_precision_quantization_amd import workloads
-from tests.gpu_util import device, to_dev_u8
+from tests.gpu_util import device, to_dev_bf16, to_dev_u8
 
 pytestmark = pytest.mark.gpu
 
@@ -31,6 +34,15 @@ def _codes_scales(rows, k, seed, lo=118, hi=136):
 
 def _cast_operand(oracle_mod, rows, k, seed):
     return oracle_mod.cast_dim0(workloads.heavy_tailed_rows(rows, k, seed=seed))
+
+
+def _blocked(oracle_mod, s, dev):
+    """(R, K/32) or (G, R, K/32) scales -> blocked bytes on the device."""
+    return to_dev_u8(oracle_mod.to_blocked(s), dev)
+
+
+def _blocked_m_groups(oracle_mod, s, ends, dev):
+    return to_dev_u8(oracle_mod.to_blocked_grouped(s, np.asarray(ends, np.int32), 0)[0], dev)
 
 
 def _check(got, want, absum, bf16, what):
@@ -51,8 +63,8 @@ def test_gemm_random_operands(oracle_mod, m, n, k, bf16):
     qa, sa = _codes_scales(m, k, m + k)
     qb, sb = _codes_scales(n, k, n + 2 * k)
     want, absum = oracle_mod.mx_gemm(qa, sa, qb, sb)
-    got = mx.mx_gemm_mxfp8(to_dev_u8(qa, dev), to_dev_u8(sa, dev), to_dev_u8(qb, dev), to_dev_u8(sb, dev),
-                           out_dtype=torch.bfloat16 if bf16 else torch.float32)
+    got = mx.mx_gemm_mxfp8(to_dev_u8(qa, dev), _blocked(oracle_mod, sa, dev), to_dev_u8(qb, dev),
+                           _blocked(oracle_mod, sb, dev), out_dtype=torch.bfloat16 if bf16 else torch.float32)
     _check(got, want, absum, bf16, "gemm %dx%dx%d" % (m, n, k))
 
 
@@ -63,8 +75,8 @@ def test_gemm_of_casts(oracle_mod):
     qa, sa = _cast_operand(oracle_mod, 384, 1024, 3)
     qb, sb = _cast_operand(oracle_mod, 256, 1024, 4)
     want, absum = oracle_mod.mx_gemm(qa, sa, qb, sb)
-    got = mx.mx_gemm_mxfp8(to_dev_u8(qa, dev), to_dev_u8(sa, dev), to_dev_u8(qb, dev), to_dev_u8(sb, dev),
-                           out_dtype=torch.float32)
+    got = mx.mx_gemm_mxfp8(to_dev_u8(qa, dev), _blocked(oracle_mod, sa, dev), to_dev_u8(qb, dev),
+                           _blocked(oracle_mod, sb, dev), out_dtype=torch.float32)
     worst = _check(got, want, absum, False, "gemm of casts")
     assert worst < 2.0 ** -11
 
@@ -93,8 +105,9 @@ def test_grouped_gemm(oracle_mod, name, m, ends):
     sb = np.stack([_codes_scales(n, k, 20 + i)[1] for i in range(g)])
     want, absum = oracle_mod.mx_gemm_grouped(qa, sa, qb, sb, np.asarray(ends, np.int32))
     out = torch.full((m, n), 12345.0, device=dev)
-    mx.mx_grouped_gemm_mxfp8(to_dev_u8(qa, dev), to_dev_u8(sa, dev), to_dev_u8(qb, dev), to_dev_u8(sb, dev),
-                             torch.tensor(ends, dtype=torch.int32, device=dev), out_dtype=torch.float32, out=out)
+    mx.mx_grouped_gemm_mxfp8(to_dev_u8(qa, dev), _blocked_m_groups(oracle_mod, sa, ends, dev), to_dev_u8(qb, dev),
+                             _blocked(oracle_mod, sb, dev), torch.tensor(ends, dtype=torch.int32, device=dev),
+                             out_dtype=torch.float32, out=out)
     torch.cuda.synchronize(dev)
     rows = ~np.isnan(want[:, 0])
     _check(out[torch.from_numpy(rows).to(dev)], want[rows], absum[rows], False, "grouped " + name)
@@ -109,7 +122,66 @@ def test_gemm_full_size_sampled(oracle_mod):
     m, n, k = 16640, 8192, 5120
     qa, sa = _codes_scales(m, k, 101)
     qb, sb = _codes_scales(n, k, 102)
-    got = mx.mx_gemm_mxfp8(to_dev_u8(qa, dev), to_dev_u8(sa, dev), to_dev_u8(qb, dev), to_dev_u8(sb, dev))
+    got = mx.mx_gemm_mxfp8(to_dev_u8(qa, dev), _blocked(oracle_mod, sa, dev), to_dev_u8(qb, dev),
+                           _blocked(oracle_mod, sb, dev))
     rows = np.sort(np.random.default_rng(5).choice(m, 24, replace=False))
     want, absum = oracle_mod.mx_gemm(qa[rows], sa[rows], qb, sb)
     _check(got[torch.from_numpy(rows).to(dev)], want, absum, True, "16640x8192x5120 sampled")
+
+
+def test_grouped_gemm_full_size_sampled(oracle_mod):
+    """The benchmark's grouped shape: M = 16640 MoE rows in 4 groups, N = 8192,
+    K = 5120, per-group weights; 24 sampled rows compared in full."""
+    dev = device()
+    m, n, k = 16640, 8192, 5120
+    _, ends = workloads.moe_activations()
+    g = len(ends)
+    qa, sa = _codes_scales(m, k, 101)
+    ops = [_codes_scales(n, k, 200 + i) for i in range(g)]
+    qb = np.stack([o[0] for o in ops])
+    sb = np.stack([o[1] for o in ops])
+    got = mx.mx_grouped_gemm_mxfp8(to_dev_u8(qa, dev), _blocked_m_groups(oracle_mod, sa, ends, dev),
+                                   to_dev_u8(qb, dev), _blocked(oracle_mod, sb, dev),
+                                   torch.from_numpy(ends).to(dev))
+    rows = np.sort(np.random.default_rng(6).choice(m, 24, replace=False))
+    grp = np.searchsorted(ends, rows, side="right")
+    for gi in np.unique(grp):
+        r = rows[grp == gi]
+        want, absum = oracle_mod.mx_gemm(qa[r], sa[r], qb[gi], sb[gi])
+        _check(got[torch.from_numpy(r).to(dev)], want, absum, True, "grouped 16640x8192x5120 group %d" % gi)
+
+
+def test_pipeline_cast_then_gemm(oracle_mod):
+    """The library's fused cast (blocked row scales) feeding the GEMM, against
+    the oracle's cast followed by the oracle's GEMM.  M = 320 and N = 224 end
+    inside a tile; K = 1056 ends a block of 32 into a 128-deep stage."""
+    dev = device()
+    xa = workloads.heavy_tailed_rows(320, 1056, seed=11)
+    xb = workloads.heavy_tailed_rows(224, 1056, seed=12)
+    qa, sa, _, _ = mx.mx_cast_dim0_dim1_blocked(to_dev_bf16(xa, dev), dim1=False, raw=True)
+    qb, sb, _, _ = mx.mx_cast_dim0_dim1_blocked(to_dev_bf16(xb, dev), dim1=False, raw=True)
+    got = mx.mx_gemm_mxfp8(qa, sa, qb, sb, out_dtype=torch.float32)
+    oqa, osa = oracle_mod.cast_dim0(xa)
+    oqb, osb = oracle_mod.cast_dim0(xb)
+    want, absum = oracle_mod.mx_gemm(oqa, osa, oqb, osb)
+    _check(got, want, absum, False, "cast -> gemm")
+
+
+def test_pipeline_grouped_cast_then_gemm(oracle_mod):
+    """MoE path: the M-grouped cast of the activations and the blocked casts
+    of the per-group weights feeding the grouped GEMM, against the oracle."""
+    dev = device()
+    ends = np.array([100, 100, 420, 640], np.int32)
+    x = workloads.heavy_tailed_rows(640, 512, seed=13)
+    ws = [workloads.heavy_tailed_rows(192, 512, seed=20 + i) for i in range(len(ends))]
+    offs = torch.from_numpy(ends).to(dev)
+    q0, s0g, _, _, _ = mx.mx_cast_dim0_dim1_mgrouped(to_dev_bf16(x, dev), offs, dim1=False, raw=True)
+    casts = [mx.mx_cast_dim0_dim1_blocked(to_dev_bf16(w, dev), dim1=False, raw=True) for w in ws]
+    qb = torch.stack([c[0] for c in casts])
+    sb = torch.cat([c[1].reshape(-1) for c in casts])
+    got = mx.mx_grouped_gemm_mxfp8(q0, s0g, qb, sb, offs, out_dtype=torch.float32)
+    oq, os_ = oracle_mod.cast_dim0(x)
+    wc = [oracle_mod.cast_dim0(w) for w in ws]
+    want, absum = oracle_mod.mx_gemm_grouped(oq, os_, np.stack([c[0] for c in wc]), np.stack([c[1] for c in wc]),
+                                             ends)
+    _check(got, want, absum, False, "grouped cast -> gemm")

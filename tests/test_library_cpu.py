@@ -116,18 +116,21 @@ def test_gemm_validation(lib):
     f = lib.mx_gemm_mxfp8
     assert f(P, P, P, P, 64, 64, 48, P, 0, None) == ERR_SHAPE        # k not a multiple of 32
     assert f(P, P, P, P, -1, 64, 64, P, 0, None) == ERR_SHAPE
-    assert f(P, P, P, P, 64, 64, (1 << 24) + 32, P, 0, None) == ERR_SHAPE
+    assert f(P, P, P, P, 64, 64, (1 << 23) + 32, P, 0, None) == ERR_SHAPE
     assert f(P, P, P, P, 64, 64, 64, P, 2, None) == ERR_SHAPE        # output type
     assert f(None, None, None, None, 0, 64, 64, None, 0, None) == OK
     assert f(P, P, None, P, 64, 64, 64, P, 0, None) == ERR_NULL
     assert f(P, P, P, P, 64, 64, 64, None, 0, None) == ERR_NULL
     assert f(P_ODD, P, P, P, 64, 64, 64, P, 0, None) == ERR_ALIGN
     assert f(P, P, P, P, 64, 64, 64, ctypes.c_void_p(0x10002), 0, None) == ERR_ALIGN   # fp32 needs 4
+    assert f(P, ctypes.c_void_p(0x10008), P, P, 64, 64, 64, P, 0, None) == ERR_ALIGN   # blocked scales: 16
+    assert f(P, P, P, ctypes.c_void_p(0x10004), 64, 64, 64, P, 0, None) == ERR_ALIGN
     g = lib.mx_grouped_gemm_mxfp8
     assert g(P, P, P, P, P, 0, 64, 64, 64, P, 1, None) == ERR_GROUPS
     assert g(P, P, P, P, None, 2, 64, 64, 64, P, 1, None) == ERR_NULL
     assert g(P, P, P, P, ctypes.c_void_p(0x10002), 2, 64, 64, 64, P, 1, None) == ERR_ALIGN
     assert g(P, P, P, P, P, 2, (1 << 31) - 200, 64, 64, P, 1, None) == ERR_SHAPE
+    assert g(P, P, P, P, P, 2, (1 << 31) - 300, 64, 64, P, 1, None) == ERR_SHAPE   # m + 256 G
 
 
 def test_rowwise_validation(lib):
