@@ -415,7 +415,8 @@ def setup_rowwise(dev, n=16384):
                 "matches_gpu": bool(ok)}
 
     config = {"workload": "mx_quantize_fp8_rowwise %dx%d bf16 (heavy-tailed rows), one bf16 scale per row"
-                          % (n, n), "rows": n, "cols": n, "elem": "e4m3fn", "scale": "bf16 per row"}
+                          % (n, n), "rows": n, "cols": n, "elem": "e4m3fn", "scale": "bf16 per row",
+              "metric": "achieved HBM GB/s (% of MI355X peak) for the bf16->fp8 row-wise cast"}
     return step, nb, timer, nb, "row-wise fp8 cast", cpu_baseline, config
 
 
@@ -452,7 +453,8 @@ def setup_tensorwise(dev, n=16384):
 
     config = {"workload": "mx_quantize_fp8_tensorwise %dx%d bf16 (heavy-tailed rows), one bf16 scale, "
                           "two-stage amax" % (n, n), "rows": n, "cols": n, "elem": "e4m3fn",
-              "scale": "bf16 per tensor"}
+              "scale": "bf16 per tensor",
+              "metric": "achieved HBM GB/s (% of MI355X peak) for the bf16->fp8 tensor-wise cast"}
     return step, nb, timer, nb, "tensor-wise fp8 cast (amax + cast launches)", cpu_baseline, config
 
 
@@ -499,6 +501,9 @@ def setup_gemm(dev, grouped=False, m=16640, n=8192, k=5120):
                           % ("mx_grouped_gemm_mxfp8" if grouped else "mx_gemm_mxfp8", m, n, k,
                              ", 4 groups along M" if grouped else ""),
               "m": m, "n": n, "k": k, "unit": "TFLOP/s", "bound": "mfma", "peak": MFMA_FP8_PEAK_TFLOPS,
+              "metric": "achieved TFLOP/s of the MX-scaled %sGEMM (%% of MI355X dense fp8 MFMA peak)"
+                        % ("grouped " if grouped else ""),
+              "dtype": "e4m3",
               "flops": flops}
     return step, flops, timer, flops, "MX GEMM" + (" grouped" if grouped else ""), None, config
 
@@ -565,6 +570,8 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     scale = 1e12 if config.get("unit") == "TFLOP/s" else 1e9
     unit = config.pop("unit", "GB/s")
+    metric = config.pop("metric", METRIC)
+    dtype = config.pop("dtype", "bf16")
     bound = config.pop("bound", "hbm")
     peak = config.pop("peak", HBM_PEAK_GBS)
     value = step_bytes / (ms_per_step * 1e-3) / scale
@@ -583,9 +590,9 @@ def main():
         log("timing the CPU oracle on a slice")
         cpu = cpu_fn()
 
-    line = {"metric": METRIC, "value": round(value, 1), "unit": unit, "n_gpus": 1,
+    line = {"metric": metric, "value": round(value, 1), "unit": unit, "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
-            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
             "data": "synthetic", "config": config, "roofline": roofline, "cpu_baseline": cpu}
     print(json.dumps(line), flush=True)
 
