@@ -35,7 +35,11 @@ Prints exactly one JSON line on stdout; progress goes to stderr.  The
 `roofline` object is for the dominant kernel (the cast): algorithmic bytes per
 launch divided by its average duration from HIP events recorded on the stream
 it runs on.  `cpu_baseline` times the CPU oracle on the same input (rank 0,
-one GPU) and checks every output byte against the GPU's.
+one GPU) and checks every output byte against the GPU's.  `cold_cache` times
+further steps one by one, each after a 512 MiB write and a 512 MiB read of
+other buffers, which evict the 256 MB Infinity Cache and the L2 (median;
+--cold-launches 0 skips it): the timed loop itself runs steps back to back,
+so a step may find part of the previous step's data still cached.
 """
 from __future__ import annotations
 
@@ -107,6 +111,36 @@ def counter_traffic():
     if not m_sha or not m_b or m_sha.group(1) != sources_digest():
         return None
     return float(m_b.group(1))
+
+
+FLUSH_BYTES = 512 << 20
+
+
+def cold_cache(step, step_bytes, launches, scale, unit, peak, dev):
+    """Each step preceded, outside its timing, by a write of one 512 MiB
+    buffer and a read of another: the write evicts the 256 MB Infinity Cache
+    and the L2, the read then evicts the write's dirty lines (their
+    write-back happens before the step) and leaves only clean, unrelated
+    lines.  One event pair per step on the current stream; the median."""
+    log("cold-cache timing: %d steps, each after a %d MiB write and a %d MiB read"
+        % (launches, FLUSH_BYTES >> 20, FLUSH_BYTES >> 20))
+    wbuf = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
+    rbuf = torch.ones(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
+    sink = torch.empty(launches, dtype=torch.int64, device=dev)
+    torch.cuda.synchronize(dev)
+    for i, (e0, e1) in enumerate(pairs):
+        wbuf.fill_(i)
+        torch.sum(rbuf, dim=0, out=sink[i])
+        e0.record()
+        step()
+        e1.record()
+    torch.cuda.synchronize(dev)
+    us = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in pairs)[launches // 2]
+    achieved = step_bytes / (us * 1e-6) / scale
+    del wbuf, rbuf
+    return {"flush_bytes": 2 * FLUSH_BYTES, "steps": launches, "step_us_median": round(us, 2),
+            "achieved": round(achieved, 1), "unit": unit, "frac": round(achieved / peak, 4)}
 
 
 class Timer:
@@ -538,6 +572,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="square16384", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-launches", type=int, default=20,
+                    help="steps timed one by one after cache-evicting traffic (0: skip)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the cast and layout kernels run on one GPU's "
@@ -585,6 +621,11 @@ def main():
                 "kernel": kern_name, "kernel_us": round(kern_ms * 1e3, 2),
                 ("algorithmic_flops" if unit == "TFLOP/s" else "algorithmic_bytes"): kern_bytes}
 
+    cold = None
+    if args.cold_launches > 0:
+        timer.reserve(args.cold_launches)   # steps that time a launch inside keep recording
+        cold = cold_cache(step, step_bytes, args.cold_launches, scale, unit, peak, dev)
+
     cpu = None
     if cpu_fn is not None and not args.no_cpu_baseline:
         log("timing the CPU oracle on a slice")
@@ -593,7 +634,8 @@ def main():
     line = {"metric": metric, "value": round(value, 1), "unit": unit, "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
-            "data": "synthetic", "config": config, "roofline": roofline, "cpu_baseline": cpu}
+            "data": "synthetic", "config": config, "roofline": roofline, "cpu_baseline": cpu,
+            "cold_cache": cold}
     print(json.dumps(line), flush=True)
 
 

@@ -254,9 +254,9 @@ __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
   // First half, entered with the first step's operands f0 read (or in
   // flight) and the stage's scales in cur: the scales of stage t + 1 are
   // loaded into nxt, and each MFMA of the first step is followed by one LDS
-  // read of the second step's operands f1; then, once this wave's loads of
-  // stage t + 1 have landed and every wave is past its reads of half st,
-  // a barrier.  Second half: each MFMA of the second step is followed by one
+  // read of the second step's operands f1.  Second half: once this wave's
+  // loads of stage t + 1 have landed and every wave is past its reads of
+  // half st, a barrier; then each MFMA of the second step is followed by one
   // load of stage t + 2 into half st and one LDS read of stage t + 1's
   // first-step operands from the other half.  A stage's loads thus have
   // about a stage of MFMA time to arrive, and no barrier stands between the
@@ -277,9 +277,6 @@ __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
       read_one(st_c, 1, q, f1a, f1b);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // all but the scale loads just issued: the loads of stage t + 1 (vmcnt)
-    __builtin_amdgcn_s_waitcnt(0x0F70 | 2);
-    lds_barrier();
   };
   auto second_half = [&](auto st_c, int kt, const Half& f1a, const Half& f1b,
                          const uint32_t (&cur_a)[kGemmWaveBlocks], const uint32_t (&cur_b)[kGemmWaveBlocks],
@@ -288,6 +285,11 @@ __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
     int xa[kGemmWaveBlocks], xb[kGemmWaveBlocks];
     step_scales(1, cur_a, xa);
     step_scales(1, cur_b, xb);
+    __builtin_amdgcn_sched_barrier(0);
+    // all but the scale loads of stage t + 1: this wave's loads of stage
+    // t + 1 (vmcnt), then every wave's
+    __builtin_amdgcn_s_waitcnt(0x0F70 | 2);
+    lds_barrier();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int q = 0; q < kGemmWaveBlocks * kGemmWaveBlocks; ++q) {
@@ -302,10 +304,11 @@ __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
   static_assert(2 * kGemmLoads == kGemmWaveBlocks * kGemmWaveBlocks, "one load per second-step MFMA");
 
   // Stages alternate between LDS halves 0 and 1 and scale registers s0 /
-  // s1.  The loop runs from a barrier to a barrier (no LDS read in flight
-  // at its head), two stages per trip; it ends with the first half of the
-  // stage after the last (an odd count: of two), past K, whose data and
-  // scales load as zero and add nothing.
+  // s1.  A trip of the loop starts with a second half, whose barrier comes
+  // before its first MFMA (so the compiler's conservative waits at the loop
+  // head cost nothing), and runs two stages; the loop ends with the first
+  // half of the stage after the last (an odd count: of two), past K, whose
+  // data and scales load as zero and add nothing.
   if (stages > 0) {
 #pragma unroll
     for (int u = 0; u < 2 * kGemmLoads; ++u) {
