@@ -106,6 +106,8 @@ def _load():
         lib.mxo_mx_gemm_grouped.restype = ctypes.c_int
         lib.mxo_num_threads.argtypes = []
         lib.mxo_num_threads.restype = ctypes.c_int
+        lib.mxo_set_num_threads.argtypes = [ctypes.c_int]
+        lib.mxo_set_num_threads.restype = None
         _lib = lib
         return lib
 
@@ -331,3 +333,8 @@ def to_blocked_grouped(s: np.ndarray, ends: np.ndarray, axis: int):
 
 def num_threads() -> int:
     return _load().mxo_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """OpenMP threads for later calls (timing only; results do not depend on it)."""
+    _load().mxo_set_num_threads(n)

@@ -651,3 +651,14 @@ int mxo_num_threads(void)
     return 1;
 #endif
 }
+
+/* Threads for the following calls (timing only: results do not depend on it). */
+void mxo_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
