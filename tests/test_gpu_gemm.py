@@ -185,3 +185,26 @@ def test_pipeline_grouped_cast_then_gemm(oracle_mod):
     want, absum = oracle_mod.mx_gemm_grouped(oq, os_, np.stack([c[0] for c in wc]), np.stack([c[1] for c in wc]),
                                              ends)
     _check(got, want, absum, False, "grouped cast -> gemm")
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_gemm_nan_code_and_scale_propagate(oracle_mod, bf16):
+    """A NaN e4m3 code (0x7F) in row 5 of A and a NaN e8m0 scale (0xFF) on
+    block 3 of row 7 of B: row 5 and column 7 of C are NaN, nothing else."""
+    dev = device()
+    m, n, k = 96, 80, 256
+    qa, sa = _codes_scales(m, k, 5)
+    qb, sb = _codes_scales(n, k, 6)
+    qa[5, 70] = 0x7F
+    sb[7, 3] = 0xFF
+    want, absum = oracle_mod.mx_gemm(qa, sa, qb, sb)
+    got = mx.mx_gemm_mxfp8(to_dev_u8(qa, dev), _blocked(oracle_mod, sa, dev), to_dev_u8(qb, dev),
+                           _blocked(oracle_mod, sb, dev), out_dtype=torch.bfloat16 if bf16 else torch.float32)
+    g = got.float().cpu().numpy()
+    nan_want = np.zeros((m, n), bool)
+    nan_want[5, :] = True
+    nan_want[:, 7] = True
+    assert np.array_equal(np.isnan(want), nan_want)        # the oracle's own reading
+    assert np.array_equal(np.isnan(g), nan_want)
+    fin = ~nan_want
+    _check(got.float()[torch.from_numpy(fin).to(dev)], want[fin], absum[fin], bf16, "finite part")
