@@ -4,8 +4,9 @@
 // against per-group (8192, 5120) weights).
 //
 //   C[m][n] = sum over k of A(m, k) * B(n, k),  A(m, k) = e4m3(qa[m][k]) *
-//   2^(sa[m][k / 32] - 127), B likewise: both operands K-major, as the dim0
-//   cast writes them (codes (rows, K), plain scales (rows, K / 32)).
+//   2^(S_A(m, k / 32) - 127), B likewise: both operands K-major, as the dim0
+//   cast writes them (codes (rows, K)), the scales S in the 128 x 4 blocked
+//   layout the casts can write directly.
 //
 // v_mfma_scale_f32_32x32x64_f8f6f4 multiplies a 32 x 64 slab of A by a
 // 64 x 32 slab of B and applies one e8m0 scale per row and 32-element block
@@ -22,26 +23,30 @@
 // Work decomposition: a 256-thread workgroup owns a 256 x 256 tile of C;
 // wave w its (w / 2, w % 2) 128 x 128 quarter = 4 x 4 MFMA blocks, whose
 // 256 accumulators live in the accumulation registers.  K advances in
-// stages of 128 bytes: the workgroup loads the stage's 256 rows of A and of
-// B (32 KiB each; every load instruction reads 32 whole 128-byte rows) into
-// registers while the MFMAs work on the previous stage, then writes them to
-// the other half of a double-buffered LDS area.  Each wave reads its MFMA
-// operands from LDS with 16-byte reads.  In LDS a row's eight 16-byte chunks
-// are permuted by an XOR of the row index (f below), so that the 16 lanes
-// of one LDS read phase, which read one chunk of 16 consecutive rows, hit
-// distinct banks, as do the writes.  Scales go straight to registers: one
-// dword (the row's four blocks of the stage) per row slab and lane.
+// stages of 128 bytes.  Every load instruction of a wave brings 8 whole
+// 128-byte rows of A or B straight from memory into LDS (buffer loads to
+// LDS, 16 bytes per lane in lane order), one stage (32 KiB of A, 32 KiB of
+// B) into one half of a double-buffered area while the MFMAs work on the
+// other.  Each wave reads its MFMA operands from LDS with 16-byte reads.
+// In LDS a row's eight 16-byte chunks are permuted by an XOR of the row
+// index (f below), applied through the loads' per-lane source offsets, so
+// that the 16 lanes of one LDS read phase, which read one chunk of 16
+// consecutive rows, hit distinct banks.  Scales come from the blocked
+// layout: a wave's 128 rows of A (or B) are one row of 128 x 4 tiles, and
+// one 16-byte load per lane and stage gives the lane its row's four block
+// scales for each of its four row slabs.
 //
 // Buffer ranges end at the tile's last row, so rows past M or N read as
-// zero; chunks past K are not loaded (zero), and their blocks take scale 1.
-// Tiles are ordered in bands of 8 tile rows, column by column, and the
-// ordered list is cut into 8 contiguous pieces, one per XCD (workgroups are
-// dealt to the XCDs round-robin), so that each XCD's L2 sees a compact
-// region of A rows and B columns.
+// zero; chunks past K load zero and their blocks' scales are the layout's
+// zero padding.  Tiles are ordered in bands of 8 tile rows, column by
+// column, and the ordered list is cut into 8 contiguous pieces, one per XCD
+// (workgroups are dealt to the XCDs round-robin), so that each XCD's L2
+// sees a compact region of A rows and B columns.
 //
 // Grouped along M (GROUPED): the tiles of group g cover its rows [lo_g,
 // hi_g) in 256-row steps from the group's padded start (the group table of
 // the blocked layouts, rebuilt from the device offsets in each workgroup);
+// A's scales are the M-grouped blocked layout (groups padded to 128 rows),
 // B and its scales are group g's (N, K) slice.  Rows past the last end are
 // not written.
 #include "mx_device.h"
