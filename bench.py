@@ -13,6 +13,10 @@ sets written in the 128x4 blocked layout by the same launch.  Other workloads
              M-grouped blocked layout itself (4 groups along M, offsets on
              the device);
   moe16640_2launch  the same from the plain cast + the M-grouped layout;
+  moe16640_both  the same cast writing the column scales K-grouped as well
+             (the weight-gradient GEMM's layout), in one launch;
+  moe16640_both_2launch  the same from the M-grouped cast + the K-grouped
+             layout of its plain column scales;
   kgroups    K-grouped layouts of (5120, 512), (8192, 4096), (2048, 4096)
              scale tensors (4 groups along K);
   experts16  dim1 cast of (16, 8192, 5120) expert weights with each
@@ -361,6 +365,61 @@ def setup_moe_2launch(dev):
     return setup_moe(dev, fused=False)
 
 
+def setup_moe_both(dev, fused=True):
+    """The MoE activations with both scale sets grouped: M-grouped row scales
+    (forward GEMM) and K-grouped column scales (weight-gradient GEMM)."""
+    bits, ends = workloads.moe_activations()
+    rows, cols = bits.shape
+    x = to_dev_bf16(bits, dev)
+    offs = torch.from_numpy(ends).to(dev)
+    g = len(ends)
+    u8 = dict(dtype=torch.uint8, device=dev)
+    q0 = torch.empty((rows, cols), **u8)
+    q1 = torch.empty((cols, rows), **u8)
+    s0g = torch.empty((rows + 128 * g, pad(cols // 32, 4)), **u8)
+    s1g = torch.empty((pad(cols, 128), pad(rows // 32, 4) + 4 * g), **u8)
+    rs = torch.empty(g + 1, dtype=torch.int64, device=dev)
+    cs = torch.empty(g + 1, dtype=torch.int64, device=dev)
+    timer = Timer(whole_step=fused)
+    if fused:
+        mx.mx_cast_dim0_dim1_grouped_blocked(x, offs, out=(q0, s0g, q1, s1g), out_row_starts=rs,
+                                             out_col_starts=cs, raw=True)
+        cast = c_call("mx_cast_dim0_dim1_grouped_blocked", x, rows, cols, offs, g, q0, s0g, rs, q1, s1g, cs)
+
+        def step():
+            with timer:
+                cast()
+
+        kb = rows * cols * 4 + s0g.numel() + s1g.numel() + 16 * (g + 1)
+        nb = kb
+        name = "cast dim0+dim1, M- and K-grouped scales"
+        label = ("mx_cast_dim0_dim1_grouped_blocked %dx%d bf16, M-grouped row scales and K-grouped column "
+                 "scales (%d groups)")
+    else:
+        s1 = torch.empty((cols, rows // 32), **u8)
+        kends = torch.from_numpy(ends // 32).to(dev)
+        mx.mx_cast_dim0_dim1_mgrouped(x, offs, out=(q0, s0g, q1, s1), out_group_starts=rs, raw=True)
+        mx.mx_scales_to_blocked_grouped(s1, kends, 1, out=s1g, out_group_starts=cs, raw=True)
+        cast = c_call("mx_cast_dim0_dim1_mgrouped", x, rows, cols, offs, g, q0, s0g, rs, q1, s1)
+        lay = c_call("mx_scales_to_blocked_grouped", s1, cols, rows // 32, kends, g, 1, s1g, cs)
+
+        def step():
+            with timer:
+                cast()
+            lay()
+
+        kb = rows * cols * 4 + s0g.numel() + s1.numel() + 8 * (g + 1)
+        nb = kb + s1.numel() + s1g.numel()
+        name = "cast dim0+dim1, M-grouped row scales"
+        label = "mx_cast_dim0_dim1_mgrouped %dx%d bf16 + K-grouped layout of the column scales (%d groups)"
+    config = {"workload": label % (rows, cols, g), "rows": rows, "cols": cols, "groups": g}
+    return step, nb, timer, kb, name, None, config
+
+
+def setup_moe_both_2launch(dev):
+    return setup_moe_both(dev, fused=False)
+
+
 def setup_kgroups(dev):
     items = []
     for shape in workloads.K_GROUP_SHAPES:
@@ -581,7 +640,8 @@ def setup_copy(dev, nbytes=1 << 30):
 
 WORKLOADS = {"square16384": setup_square, "square16384_3launch": setup_square_3launch,
              "moe16640": setup_moe, "moe16640_2launch": setup_moe_2launch, "kgroups": setup_kgroups, "rowwise16384": setup_rowwise,
-             "tensorwise16384": setup_tensorwise, "gemm16640": setup_gemm, "ggemm16640": setup_ggemm,
+             "tensorwise16384": setup_tensorwise, "moe16640_both": setup_moe_both,
+             "moe16640_both_2launch": setup_moe_both_2launch, "gemm16640": setup_gemm, "ggemm16640": setup_ggemm,
              "experts16": setup_experts, "experts16_2launch": setup_experts_2launch, "copy": setup_copy}
 
 

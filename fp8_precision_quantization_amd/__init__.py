@@ -12,6 +12,7 @@ from ._binding import (  # noqa: F401
     mx_blocked_grouped_bytes,
     mx_cast_dim0_dim1,
     mx_cast_dim0_dim1_blocked,
+    mx_cast_dim0_dim1_grouped_blocked,
     mx_cast_dim0_dim1_mgrouped,
     mx_cast_dim1_3d,
     mx_cast_dim1_3d_blocked,

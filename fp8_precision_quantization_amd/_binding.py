@@ -34,6 +34,8 @@ SIGNATURES = {
     "mx_cast_dim0_dim1_blocked": ([_vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "mx_cast_dim1_3d_blocked": ([_vp, _i64, _i64, _i64, _vp, _vp, _vp], ctypes.c_int),
     "mx_cast_dim0_dim1_mgrouped": ([_vp, _i64, _i64, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
+    "mx_cast_dim0_dim1_grouped_blocked": ([_vp, _i64, _i64, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
+                                          ctypes.c_int),
     "mx_quantize_fp8_rowwise": ([_vp, _i64, _i64, _vp, _vp, _vp], ctypes.c_int),
     "mx_tensorwise_workspace_bytes": ([_i64], _i64),
     "mx_quantize_fp8_tensorwise": ([_vp, _i64, _vp, _vp, _vp, _i64, _vp], ctypes.c_int),
@@ -208,6 +210,41 @@ def mx_cast_dim0_dim1_mgrouped(x, group_end_offsets, dim1: bool = True, out=None
     r0 = _views(q0, s0, raw)
     r1 = _views(q1, s1, raw) if dim1 else (None, None)
     return r0[0], r0[1], starts, r1[0], r1[1]
+
+
+def _starts_out(t, g, dev, name):
+    if t is None:
+        return torch.empty(g + 1, dtype=torch.int64, device=dev)
+    if t.dtype != torch.int64 or t.numel() != g + 1 or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous int64 tensor of G + 1" % name)
+    return t
+
+
+def mx_cast_dim0_dim1_grouped_blocked(x, group_end_offsets, out=None, out_row_starts=None, out_col_starts=None,
+                                      raw: bool = False):
+    """MoE activations grouped along M, both scale sets in grouped blocked
+    layouts: the row scales M-grouped ((R + 128 G, ceil4(C/32)), as
+    mx_cast_dim0_dim1_mgrouped) and the column scales K-grouped along their
+    32-row blocks ((ceil128(C), ceil4(R/32) + 4 G), what
+    mx_scales_to_blocked_grouped(s_col, offsets // 32, 1) gives).  Returns
+    (q_row, s_row_grouped, row_starts, q_col, s_col_grouped, col_starts)."""
+    _bf16_input(x, 2, "x")
+    offs = _offsets(group_end_offsets)
+    rows, cols = x.shape
+    g = offs.numel()
+    o = out if out is not None else (None, None, None, None)
+    q0 = _out(o[0], (rows, cols), x.device, "q_row")
+    s0 = _out(o[1], (rows + 128 * g, _pad(cols // MX_BLOCK, 4)), x.device, "s_row_grouped")
+    q1 = _out(o[2], (cols, rows), x.device, "q_col")
+    s1 = _out(o[3], (_pad(cols, 128), _pad(rows // MX_BLOCK, 4) + 4 * g), x.device, "s_col_grouped")
+    rs = _starts_out(out_row_starts, g, x.device, "out_row_starts")
+    cs = _starts_out(out_col_starts, g, x.device, "out_col_starts")
+    _check(lib().mx_cast_dim0_dim1_grouped_blocked(_ptr(x), rows, cols, _ptr(offs), g, _ptr(q0), _ptr(s0),
+                                                   _ptr(rs), _ptr(q1), _ptr(s1), _ptr(cs), _stream(x.device)),
+           "mx_cast_dim0_dim1_grouped_blocked")
+    r0 = _views(q0, s0, raw)
+    r1 = _views(q1, s1, raw)
+    return r0[0], r0[1], rs, r1[0], r1[1], cs
 
 
 def mx_cast_dim1_3d_blocked(w, out=None, raw: bool = False):

@@ -139,6 +139,48 @@ mx_status mx_cast_dim0_dim1_mgrouped(const void* x, int64_t rows, int64_t cols,
                                            d1 ? q_col : nullptr, d1 ? s_col : nullptr, stream));
 }
 
+mx_status mx_cast_dim0_dim1_grouped_blocked(const void* x, int64_t rows, int64_t cols,
+                                            const int32_t* group_end_offsets, int32_t num_groups, uint8_t* q_row,
+                                            uint8_t* s_row_grouped, int64_t* row_group_starts, uint8_t* q_col,
+                                            uint8_t* s_col_grouped, int64_t* col_group_starts,
+                                            hipStream_t stream) {
+  if (rows < 0 || cols < 0 || rows % MX_BLOCK != 0 || cols % MX_BLOCK != 0 || rows > kMaxExtent ||
+      cols > kMaxCastCols || (cols == 0 && rows > 0))
+    return MX_ERR_SHAPE;
+  if (num_groups < 1 || num_groups > MX_MAX_GROUPS)
+    return MX_ERR_GROUPS;
+  if (rows + 128 * (int64_t)num_groups >= INT_MAX || cols + 128 >= INT_MAX)
+    return MX_ERR_SHAPE;
+  const int64_t bytes0 = mx_blocked_grouped_bytes(rows, cols / MX_BLOCK, num_groups, 0);
+  const int64_t bytes1 = mx_blocked_grouped_bytes(cols, rows / MX_BLOCK, num_groups, 1);
+  if (group_end_offsets == nullptr || (bytes0 > 0 && s_row_grouped == nullptr) ||
+      (bytes1 > 0 && s_col_grouped == nullptr))
+    return MX_ERR_NULL;
+  if (!aligned(group_end_offsets, 4) || (s_row_grouped != nullptr && !aligned(s_row_grouped, 16)) ||
+      (s_col_grouped != nullptr && !aligned(s_col_grouped, 16)) ||
+      (row_group_starts != nullptr && !aligned(row_group_starts, 8)) ||
+      (col_group_starts != nullptr && !aligned(col_group_starts, 8)))
+    return MX_ERR_ALIGN;
+  if (rows == 0) {
+    // no codes and every group empty: both grouped buffers are all padding
+    hipError_t e = mx::launch_blocked_grouped(nullptr, rows, cols / MX_BLOCK, group_end_offsets, num_groups, 0,
+                                              s_row_grouped, bytes0, row_group_starts, stream);
+    if (e == hipSuccess)
+      e = mx::launch_blocked_grouped(nullptr, cols, rows / MX_BLOCK, group_end_offsets, num_groups, 1,
+                                     s_col_grouped, bytes1, col_group_starts, stream);
+    return from_hip(e);
+  }
+  if (x == nullptr || q_row == nullptr || q_col == nullptr)
+    return MX_ERR_NULL;
+  if (mx::cast_grid_blocks(rows, cols) > kMaxGridBlocks)
+    return MX_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(q_row, 8) || !aligned(q_col, 16))
+    return MX_ERR_ALIGN;
+  return from_hip(mx::launch_cast_grouped_blocked(static_cast<const uint16_t*>(x), rows, cols, group_end_offsets,
+                                                  num_groups, q_row, s_row_grouped, bytes0, row_group_starts,
+                                                  q_col, s_col_grouped, bytes1, col_group_starts, stream));
+}
+
 mx_status mx_cast_dim1_3d(const void* w, int64_t experts, int64_t n, int64_t k, uint8_t* q,
                           uint8_t* s, hipStream_t stream) {
   if (experts < 0 || n < 0 || k < 0 || n % MX_BLOCK != 0 || k % MX_BLOCK != 0 ||

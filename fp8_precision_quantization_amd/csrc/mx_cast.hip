@@ -229,7 +229,38 @@ struct CastArgs {
   int32_t groups;
   int64_t* out_starts;
   int64_t s0_bytes;
+  // K-grouped dim1 scales (the same groups of rows, in 32-row blocks): the
+  // padded column starts to write (device, may be null), the output's size.
+  int64_t* s1_starts;
+  int64_t s1_bytes;
 };
+
+// Column starts of the K-grouped dim1 scales: group g covers scale columns
+// (32-row blocks) [lo_g / 32, hi_g / 32) of the clamped row ranges, padded
+// to a multiple of 4; kstart[g] = sum of the earlier padded widths, kstart[G]
+// the total.  Wave 0 fills it after the row table.
+struct KStarts {
+  int32_t start[MX_MAX_GROUPS + 1];
+};
+struct NoKStarts {};
+
+__device__ inline void build_kstarts(const GroupTable& t, int groups, KStarts& k) {
+  const int lane = threadIdx.x & 63;
+  const int per = (groups + 63) / 64;
+  const int g0 = min(lane * per, groups), g1 = min(g0 + per, groups);
+  int32_t local = 0;
+  for (int g = g0; g < g1; ++g)
+    local += (t.hi[g] / 32 - t.lo[g] / 32 + 3) / 4 * 4;
+  const int32_t incl = wave_incl_sum(local, lane);
+  int32_t run = incl - local;
+  for (int g = g0; g < g1; ++g) {
+    k.start[g] = run;
+    run += (t.hi[g] / 32 - t.lo[g] / 32 + 3) / 4 * 4;
+  }
+  const int32_t total = __shfl(incl, 63);
+  if (lane == 0)
+    k.start[groups] = total;
+}
 
 struct Stage {
   uint4 q1[kTileCols * kSlots];   // dim1 codes, 128 rows x 256 columns
@@ -318,6 +349,116 @@ __device__ __forceinline__ void mgrouped_scales(const CastArgs& a, const GroupTa
   }
 }
 
+// Group of scale column (32-row block) b under the K-group reading: the g
+// with lo_g / 32 <= b < hi_g / 32, or -1 past the last group.
+__device__ __forceinline__ int kgroup_of(const GroupTable& t, int groups, int64_t b) {
+  if (groups <= 0 || b >= t.hi[groups - 1] / 32)
+    return -1;
+  int lo = 0, hi = groups - 1;  // smallest g with hi[g] / 32 > b lies in [lo, hi]
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (t.hi[mid] / 32 > b)
+      hi = mid;
+    else
+      lo = mid + 1;
+  }
+  return lo;
+}
+
+// Byte (c, p) of group g's blocked matrix in the K-grouped layout: the
+// group's matrix (ceil128(C) rows x its padded width wp columns) starts at
+// ceil128(C) * kstart[g].
+__device__ __forceinline__ int64_t kgroup_index(int64_t cpad, int64_t kstart, int64_t wp, int64_t c, int64_t p) {
+  return cpad * kstart + ((c >> 7) * (wp >> 2) + (p >> 2)) * 512 + (c & 31) * 16 + ((c & 127) >> 5) * 4 + (p & 3);
+}
+
+// Store phase of the K-grouped dim1 scales of tile (rt, ct): s1img[col] holds
+// the four block scales (blocks 4 rt .. 4 rt + 3) of x column tc + col.
+// - Each column's bytes go to their groups' matrices: one 4-byte store when
+//   the tile's four blocks open a 4-column block of one group, else byte by
+//   byte.
+// - The padding columns of a group whose last block is in this row of
+//   tiles are zeroed for this tile's columns.
+// - The last column of tiles also zeroes the padding rows (x columns C ..
+//   ceil128(C) - 1) of this row of tiles' blocks and of those padding
+//   columns.
+// - Bytes past the padded total are zeroed, split over the workgroups of
+//   the last row of tiles.
+__device__ inline void kgrouped_scales(const CastArgs& a, const GroupTable& table, const KStarts& ks,
+                                       const uint32_t* s1img, uint32_t rt, uint32_t ct, int valid_rows,
+                                       int valid_cols) {
+  const int t = threadIdx.x;
+  const int64_t C = a.cols;
+  const int64_t cpad = (C + 127) / 128 * 128;
+  const int64_t tc = (int64_t)ct * kTileCols;
+  const int nblk = valid_rows / 32;
+  const int64_t b0 = 4 * (int64_t)rt;
+  // the tile's blocks: group, local column, padded width (uniform)
+  int bg[kWaves];
+  int64_t bp[kWaves], bw[kWaves];
+#pragma unroll
+  for (int j = 0; j < kWaves; ++j) {
+    bg[j] = j < nblk ? kgroup_of(table, a.groups, b0 + j) : -1;
+    bp[j] = bg[j] >= 0 ? b0 + j - table.lo[bg[j]] / 32 : 0;
+    bw[j] = bg[j] >= 0 ? (table.hi[bg[j]] / 32 - table.lo[bg[j]] / 32 + 3) / 4 * 4 : 0;
+  }
+  const bool whole = nblk == kWaves && bg[0] >= 0 && bg[0] == bg[kWaves - 1] && (bp[0] & 3) == 0;
+  if (t < valid_cols) {
+    const int64_t c = tc + t;
+    const uint32_t v = s1img[t];
+    if (whole) {
+      *reinterpret_cast<uint32_t*>(a.s1 + kgroup_index(cpad, ks.start[bg[0]], bw[0], c, bp[0])) = v;
+    } else {
+#pragma unroll
+      for (int j = 0; j < kWaves; ++j)
+        if (bg[j] >= 0)
+          a.s1[kgroup_index(cpad, ks.start[bg[j]], bw[j], c, bp[j])] = (uint8_t)(v >> (8 * j));
+    }
+  }
+  // groups whose last block lies in this row of tiles: their padding columns
+  const bool last_ct = ct == a.col_tiles - 1;
+  for (int g = max(0, kgroup_of(table, a.groups, b0)); g >= 0 && g < a.groups; ++g) {
+    const int64_t klo = table.lo[g] / 32, khi = table.hi[g] / 32;
+    if (khi > b0 + nblk)
+      break;  // this group (and every later one) ends further down
+    if (khi <= b0 || khi == klo)
+      continue;  // ends above this row of tiles, or has no blocks
+    const int64_t w = khi - klo, wp = (w + 3) / 4 * 4;
+    // padding columns w .. wp - 1, this tile's columns (and, from the last
+    // column of tiles, the padding rows)
+    const int64_t c_end = last_ct ? cpad : tc + valid_cols;
+    for (int64_t c = tc + t; c < c_end; c += kWaves * 64)
+      for (int64_t p = w; p < wp; ++p)
+        a.s1[kgroup_index(cpad, ks.start[g], wp, c, p)] = 0;
+  }
+  // padding rows of this row of tiles' blocks
+  if (last_ct && cpad > C) {
+    for (int64_t c = C + t; c < cpad; c += kWaves * 64)
+#pragma unroll
+      for (int j = 0; j < kWaves; ++j)
+        if (bg[j] >= 0)
+          a.s1[kgroup_index(cpad, ks.start[bg[j]], bw[j], c, bp[j])] = 0;
+  }
+  // bytes past the padded total (whole 512-byte tiles from there on)
+  if (rt == a.row_tiles - 1) {
+    const int64_t lo = cpad * ks.start[a.groups];
+    const int64_t chunk = ((a.s1_bytes - lo + a.col_tiles - 1) / a.col_tiles + 15) / 16 * 16;
+    const int64_t e0 = lo + (int64_t)ct * chunk, e1 = min(a.s1_bytes, e0 + chunk);
+    for (int64_t e = e0 + 16 * t; e < e1; e += 16 * kWaves * 64) {
+      if (e + 16 <= e1) {
+        *reinterpret_cast<uint4*>(a.s1 + e) = make_uint4(0, 0, 0, 0);
+      } else {
+        for (int64_t j = e; j < e1; ++j)
+          a.s1[j] = 0;
+      }
+    }
+  }
+  if (blockIdx.x == 0 && a.s1_starts != nullptr) {
+    for (int g = t; g <= a.groups; g += kWaves * 64)
+      a.s1_starts[g] = ks.start[g];
+  }
+}
+
 // rows_per_seg: the rows of x form consecutive segments of this many rows
 // (3D weights: one per expert; 2D: one segment).  Segment e's dim1 output is
 // a (cols, rows_per_seg) matrix at e * cols * rows_per_seg, its scales a
@@ -334,12 +475,16 @@ __device__ __forceinline__ void mgrouped_scales(const CastArgs& a, const GroupTa
 // 8 scale bytes of a tile go to its output row as two 4-byte stores; the
 // workgroup holding a group's last row zeroes the group's padding rows, and
 // the last row of tiles zeroes the bytes past the padded total.
-template <bool DIM0, bool DIM1, bool BLK, bool MGRP>
+// KGRP (with MGRP and DIM1): the dim1 scales are written in the K-grouped
+// blocked layout of the same groups counted in 32-row blocks (kgrouped_scales).
+template <bool DIM0, bool DIM1, bool BLK, bool MGRP, bool KGRP = false>
 __global__ __launch_bounds__(256) void cast_kernel(CastArgs a) {
+  static_assert(!KGRP || (MGRP && DIM1 && !BLK), "K-grouped dim1 scales come with the M-grouped cast");
   __shared__ std::conditional_t<DIM1, Stage, NoStage> stage;
   // the tile's dim0 scales: two blocked tiles (BLK) or a plain image (MGRP)
   __shared__ uint8_t s0_blk[(DIM0 && (BLK || MGRP)) ? 2 * 512 : 1];
   __shared__ std::conditional_t<MGRP, GroupTable, NoTable> table;
+  __shared__ std::conditional_t<KGRP, KStarts, NoKStarts> kstarts;
 
   uint32_t rt, ct;
   if (!tile_of(blockIdx.x, a.row_tiles, a.col_tiles, a.per_xcd, a.row_group, rt, ct))
@@ -445,8 +590,11 @@ __global__ __launch_bounds__(256) void cast_kernel(CastArgs a) {
   }
 
   if constexpr (MGRP) {
-    if (wave == 0)
+    if (wave == 0) {
       build_group_table(a.ends, a.groups, (int32_t)a.rows, kTileRows, table);
+      if constexpr (KGRP)
+        build_kstarts(table, a.groups, kstarts);
+    }
   }
   if constexpr (DIM1 || (DIM0 && (BLK || MGRP))) {
     // Every wave reaches the barrier; it orders LDS only (no wait on
@@ -510,6 +658,8 @@ __global__ __launch_bounds__(256) void cast_kernel(CastArgs a) {
           store_line_nt(a.s1 + seg0 * a.seg_blk_bytes + (rb * a.ncb1 + off0 / 128) * 512 + i * 16, v);
         }
       }
+    } else if constexpr (KGRP) {
+      kgrouped_scales(a, table, kstarts, st.s1, rt, ct, valid_rows, valid_cols);
     } else {
       // Plain scales: one thread per column, the four 32-row blocks of the band.
       const int col = threadIdx.x;
@@ -561,6 +711,8 @@ static CastArgs cast_args(const uint16_t* x, int64_t rows, int64_t cols, int64_t
   a.groups = 0;
   a.out_starts = nullptr;
   a.s0_bytes = 0;
+  a.s1_starts = nullptr;
+  a.s1_bytes = 0;
   a.ncb0 = (cols / 32 + 3) / 4;
   a.ncb1 = (rows_per_seg / 32 + 3) / 4;
   a.seg_blk_bytes = (cols + 127) / 128 * 128 * (a.ncb1 * 4);
@@ -574,10 +726,10 @@ int64_t cast_grid_blocks(int64_t rows, int64_t cols) {
   return blocks;
 }
 
-template <bool DIM0, bool DIM1, bool BLK, bool MGRP = false>
+template <bool DIM0, bool DIM1, bool BLK, bool MGRP = false, bool KGRP = false>
 static hipError_t launch_cast(const CastArgs& a, int64_t blocks, hipStream_t stream) {
-  hipLaunchKernelGGL((cast_kernel<DIM0, DIM1, BLK, MGRP>), dim3((unsigned)blocks), dim3(kWaves * 64), 0, stream,
-                     a);
+  hipLaunchKernelGGL((cast_kernel<DIM0, DIM1, BLK, MGRP, KGRP>), dim3((unsigned)blocks), dim3(kWaves * 64), 0,
+                     stream, a);
   return hipGetLastError();
 }
 
@@ -613,6 +765,21 @@ hipError_t launch_cast_mgrouped(const uint16_t* x, int64_t rows, int64_t cols, c
   if (q1 != nullptr)
     return launch_cast<true, true, false, true>(a, blocks, stream);
   return launch_cast<true, false, false, true>(a, blocks, stream);
+}
+
+hipError_t launch_cast_grouped_blocked(const uint16_t* x, int64_t rows, int64_t cols, const int32_t* ends,
+                                       int32_t groups, uint8_t* q0, uint8_t* s0_grouped, int64_t s0_bytes,
+                                       int64_t* row_starts, uint8_t* q1, uint8_t* s1_grouped, int64_t s1_bytes,
+                                       int64_t* col_starts, hipStream_t stream) {
+  int64_t blocks;
+  CastArgs a = cast_args(x, rows, cols, rows, q0, s0_grouped, q1, s1_grouped, false, &blocks);
+  a.ends = ends;
+  a.groups = groups;
+  a.out_starts = row_starts;
+  a.s0_bytes = s0_bytes;
+  a.s1_starts = col_starts;
+  a.s1_bytes = s1_bytes;
+  return launch_cast<true, true, false, true, true>(a, blocks, stream);
 }
 
 }  // namespace mx

@@ -20,6 +20,10 @@ int64_t cast_grid_blocks(int64_t rows, int64_t cols);
 hipError_t launch_cast_mgrouped(const uint16_t* x, int64_t rows, int64_t cols, const int32_t* ends,
                                 int32_t groups, uint8_t* q0, uint8_t* s0_grouped, int64_t s0_bytes,
                                 int64_t* out_starts, uint8_t* q1, uint8_t* s1, hipStream_t stream);
+hipError_t launch_cast_grouped_blocked(const uint16_t* x, int64_t rows, int64_t cols, const int32_t* ends,
+                                       int32_t groups, uint8_t* q0, uint8_t* s0_grouped, int64_t s0_bytes,
+                                       int64_t* row_starts, uint8_t* q1, uint8_t* s1_grouped, int64_t s1_bytes,
+                                       int64_t* col_starts, hipStream_t stream);
 
 hipError_t launch_blocked_batched(const uint8_t* s, int64_t batch, int64_t rows, int64_t cols,
                                   uint8_t* out, hipStream_t stream);

@@ -152,6 +152,44 @@ MX_API mx_status mx_cast_dim0_dim1_mgrouped(const void* x, int64_t rows, int64_t
                                             uint8_t* q_col, uint8_t* s_col, hipStream_t stream);
 
 /*
+ * The MoE activation cast with BOTH scale sets written in their grouped
+ * blocked layouts, for the two grouped GEMMs of MoE training: the row scales
+ * M-grouped as by mx_cast_dim0_dim1_mgrouped (the forward GEMM, grouped
+ * along its M), and the column scales K-grouped -- the groups of rows are
+ * the groups along the K dimension of the weight-gradient GEMM, which
+ * contracts over the tokens ("[mxfp8 moe training] parallelize along col
+ * blocks in scale blocked format kernel for groups along K"; "triton kernel
+ * to cast to mx across dim0 and dim1", future improvement 2: swizzled scales
+ * from the cast).  One read of x, no layout pass of its own.
+ *   group_end_offsets  DEVICE int32 [num_groups], cumulative END rows,
+ *                      clamped on the device as by
+ *                      mx_scales_to_blocked_grouped.
+ *   q_row, s_row_grouped, row_group_starts   as for
+ *                      mx_cast_dim0_dim1_mgrouped (q_row required).
+ *   q_col              col-major codes (cols, rows), 16-byte aligned
+ *                      (required).
+ *   s_col_grouped      mx_blocked_grouped_bytes(cols, rows / 32, num_groups,
+ *                      1) bytes, 16-byte aligned, every byte written: what
+ *                      mx_scales_to_blocked_grouped(s_col, ends_k, group_axis
+ *                      1) makes of the plain (cols, rows / 32) column scales
+ *                      with ends_k[g] = end_g / 32 rounded down (a 32-row
+ *                      block belongs to the group it falls in whole; group
+ *                      ends at multiples of 32 keep every block whole).
+ *   col_group_starts   DEVICE int64 [num_groups + 1] or NULL: padded start
+ *                      column of each group, then the padded total.
+ * Shapes as for mx_cast_dim0_dim1, plus cols > 0 when rows > 0 (else
+ * MX_ERR_SHAPE); 1 <= num_groups <= MX_MAX_GROUPS (else MX_ERR_GROUPS), rows
+ * + 128 * num_groups < 2^31.  With rows 0 only the (all-zero) grouped
+ * buffers and the starts are written.
+ */
+MX_API mx_status mx_cast_dim0_dim1_grouped_blocked(const void* x, int64_t rows, int64_t cols,
+                                                   const int32_t* group_end_offsets, int32_t num_groups,
+                                                   uint8_t* q_row, uint8_t* s_row_grouped,
+                                                   int64_t* row_group_starts, uint8_t* q_col,
+                                                   uint8_t* s_col_grouped, int64_t* col_group_starts,
+                                                   hipStream_t stream);
+
+/*
  * dim1 cast of 3D expert weights, expert by expert.
  *   w  bf16 (experts, n, k) contiguous; 16-byte aligned.
  *   q  e4m3 (experts, k, n): expert e's (n, k) matrix cast in blocks of 32

@@ -33,7 +33,7 @@ def declared_functions():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"mx_status_string", "mx_cast_dim0_dim1", "mx_cast_dim0_dim1_blocked",
-                          "mx_cast_dim0_dim1_mgrouped",
+                          "mx_cast_dim0_dim1_mgrouped", "mx_cast_dim0_dim1_grouped_blocked",
                           "mx_cast_dim1_3d", "mx_cast_dim1_3d_blocked", "mx_quantize_fp8_rowwise",
                           "mx_tensorwise_workspace_bytes", "mx_quantize_fp8_tensorwise",
                           "mx_gemm_mxfp8", "mx_grouped_gemm_mxfp8",
@@ -110,6 +110,22 @@ def test_mgrouped_cast_validation(lib):
     assert f(P, 64, 64, P, 4, P, P, ctypes.c_void_p(0x10004), P, P, None) == ERR_ALIGN
     assert f(P_ODD, 64, 64, P, 4, P, P, P, None, None, None) == ERR_ALIGN
     assert f(P, (1 << 31) - 128 * 4, 64, P, 4, P, P, P, P, P, None) == ERR_SHAPE
+
+
+def test_grouped_blocked_cast_validation(lib):
+    f = lib.mx_cast_dim0_dim1_grouped_blocked
+    # x, rows, cols, ends, G, q_row, s_row_grouped, row_starts, q_col, s_col_grouped, col_starts, stream
+    assert f(P, 33, 64, P, 4, P, P, P, P, P, P, None) == ERR_SHAPE
+    assert f(P, 64, 0, P, 4, P, P, P, P, P, P, None) == ERR_SHAPE           # cols 0 with rows
+    assert f(P, 64, 64, P, 0, P, P, P, P, P, P, None) == ERR_GROUPS
+    assert f(P, 64, 64, None, 4, P, P, P, P, P, P, None) == ERR_NULL        # offsets
+    assert f(P, 64, 64, P, 4, P, None, P, P, P, P, None) == ERR_NULL        # row scales
+    assert f(P, 64, 64, P, 4, P, P, P, P, None, P, None) == ERR_NULL        # column scales
+    assert f(P, 64, 64, P, 4, P, P, P, None, P, P, None) == ERR_NULL        # q_col is required
+    assert f(P, 64, 64, P, 4, None, P, P, P, P, P, None) == ERR_NULL        # q_row is required
+    assert f(P, 64, 64, P, 4, P, P, P, P, ctypes.c_void_p(0x10008), P, None) == ERR_ALIGN
+    assert f(P, 64, 64, P, 4, P, P, P, P, P, ctypes.c_void_p(0x10004), None) == ERR_ALIGN
+    assert f(P, (1 << 31) - 128 * 4, 64, P, 4, P, P, P, P, P, P, None) == ERR_SHAPE
 
 
 def test_gemm_validation(lib):
@@ -219,7 +235,8 @@ def test_python_binding_rejects_cpu_tensors_everywhere():
                  lambda: mx.mx_cast_dim1_3d_blocked(x.view(1, 32, 32)),
                  lambda: mx.mx_quantize_fp8_rowwise(x),
                  lambda: mx.mx_quantize_fp8_tensorwise(x),
-                 lambda: mx.mx_cast_dim0_dim1_mgrouped(x, torch.tensor([32], dtype=torch.int32))):
+                 lambda: mx.mx_cast_dim0_dim1_mgrouped(x, torch.tensor([32], dtype=torch.int32)),
+                 lambda: mx.mx_cast_dim0_dim1_grouped_blocked(x, torch.tensor([32], dtype=torch.int32))):
         with pytest.raises(ValueError):
             call()
 
