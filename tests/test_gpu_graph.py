@@ -36,6 +36,9 @@ def _calls(dev):
                   torch.empty(cols, rows, **u8), torch.empty(cols, rows // 32, **u8)),
         "blk": (torch.empty(rows, cols, **u8), torch.empty(rows, cols // 32, **u8),   # 1024 and 512: no padding
                 torch.empty(cols, rows, **u8), torch.empty(cols, rows // 32, **u8)),
+        "gb": (torch.empty(rows, cols, **u8), torch.empty(rows + 128 * g, cols // 32, **u8),
+               torch.empty(cols, rows, **u8), torch.empty(cols, rows // 32 + 4 * g, **u8),
+               torch.empty(g + 1, dtype=torch.int64, device=dev), torch.empty(g + 1, dtype=torch.int64, device=dev)),
         "kg": (torch.empty(cols, rows // 32 + 4 * g, **u8),   # (ceil128(512), ceil4(32) + 4 G)
                torch.empty(g + 1, dtype=torch.int64, device=dev)),
         "tw": (torch.empty(rows, cols, **u8), torch.empty(1, dtype=torch.int16, device=dev),
@@ -55,6 +58,9 @@ def _calls(dev):
         mg = outs["mg"]
         mx.mx_cast_dim0_dim1_mgrouped(x, offs, out=mg[:2] + mg[3:], out_group_starts=mg[2], raw=True)
         mx.mx_cast_dim0_dim1(x, out=outs["plain"], raw=True)
+        gb = outs["gb"]
+        mx.mx_cast_dim0_dim1_grouped_blocked(x, offs, out=gb[:4], out_row_starts=gb[4], out_col_starts=gb[5],
+                                             raw=True)
         mx.mx_cast_dim0_dim1_blocked(x, out=outs["blk"], raw=True)
         kg = outs["kg"]
         mx.mx_scales_to_blocked_grouped(mg[4], kends, 1, out=kg[0], out_group_starts=kg[1], raw=True)
