@@ -29,6 +29,8 @@ sets written in the 128x4 blocked layout by the same launch.  Other workloads
   gemm16640  the MX-scaled GEMM that consumes the casts: M = 16640, N =
              8192, K = 5120, bf16 out (TFLOP/s against the MFMA roofline);
   ggemm16640 the same grouped along M (4 groups, per-group weights);
+  kggemm16640  the weight-gradient GEMM grouped along K: 4 outputs of
+             (8192, 5120), K = the 16640 tokens split in 4 groups;
   copy       a plain device-to-device copy of 1 GiB (counter calibration).
 
 Each workload's calls are validated once through the Python binding; the
@@ -625,6 +627,37 @@ def setup_ggemm(dev):
     return setup_gemm(dev, grouped=True)
 
 
+def setup_kggemm(dev, m=8192, n=5120, k=16640):
+    """The MoE weight-gradient GEMM: dW_g (8192, 5120) = dY_g^T X_g over each
+    group's tokens, the 16640 tokens split as the MoE workload splits them."""
+    log("generating MX operands")
+    _, ends = workloads.moe_activations()
+    g = len(ends)
+    offs = torch.from_numpy(ends).to(dev)
+    kends = torch.from_numpy(ends // 32).to(dev)
+    qa, sa = _mx_operands(m, k, 111, dev)
+    qb, sb = _mx_operands(n, k, 112, dev)
+    sa = mx.mx_scales_to_blocked_grouped(sa, kends, 1, raw=True)[0]
+    sb = mx.mx_scales_to_blocked_grouped(sb, kends, 1, raw=True)[0]
+    c = torch.empty((g, m, n), dtype=torch.bfloat16, device=dev)
+    timer = Timer(whole_step=True)
+    mx.mx_kgrouped_gemm_mxfp8(qa, sa, qb, sb, offs, out=c)
+    call = c_call("mx_kgrouped_gemm_mxfp8", qa, sa, qb, sb, offs, g, m, n, k, c, 1)
+
+    def step():
+        with timer:
+            call()
+
+    flops = 2 * m * n * k
+    config = {"workload": "mx_kgrouped_gemm_mxfp8 M=%d N=%d K=%d tokens in %d groups along K, e4m3 x e4m3 with "
+                          "e8m0 block scales (K-grouped blocked layout), bf16 out" % (m, n, k, g),
+              "m": m, "n": n, "k": k, "groups": g, "unit": "TFLOP/s", "bound": "mfma",
+              "peak": MFMA_FP8_PEAK_TFLOPS,
+              "metric": "achieved TFLOP/s of the MX-scaled GEMM grouped along K (% of MI355X dense fp8 MFMA peak)",
+              "dtype": "e4m3", "flops": flops}
+    return step, flops, timer, flops, "MX GEMM grouped along K", None, config
+
+
 def setup_copy(dev, nbytes=1 << 30):
     a = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
     b = torch.empty_like(a)
@@ -641,7 +674,7 @@ def setup_copy(dev, nbytes=1 << 30):
 WORKLOADS = {"square16384": setup_square, "square16384_3launch": setup_square_3launch,
              "moe16640": setup_moe, "moe16640_2launch": setup_moe_2launch, "kgroups": setup_kgroups, "rowwise16384": setup_rowwise,
              "tensorwise16384": setup_tensorwise, "moe16640_both": setup_moe_both,
-             "moe16640_both_2launch": setup_moe_both_2launch, "gemm16640": setup_gemm, "ggemm16640": setup_ggemm,
+             "moe16640_both_2launch": setup_moe_both_2launch, "gemm16640": setup_gemm, "ggemm16640": setup_ggemm, "kggemm16640": setup_kggemm,
              "experts16": setup_experts, "experts16_2launch": setup_experts_2launch, "copy": setup_copy}
 
 

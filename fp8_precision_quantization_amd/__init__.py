@@ -18,6 +18,7 @@ from ._binding import (  # noqa: F401
     mx_cast_dim1_3d_blocked,
     mx_gemm_mxfp8,
     mx_grouped_gemm_mxfp8,
+    mx_kgrouped_gemm_mxfp8,
     mx_quantize_fp8_rowwise,
     mx_quantize_fp8_tensorwise,
     mx_scales_to_blocked,

@@ -41,6 +41,7 @@ SIGNATURES = {
     "mx_quantize_fp8_tensorwise": ([_vp, _i64, _vp, _vp, _vp, _i64, _vp], ctypes.c_int),
     "mx_gemm_mxfp8": ([_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _i32, _vp], ctypes.c_int),
     "mx_grouped_gemm_mxfp8": ([_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _i32, _vp], ctypes.c_int),
+    "mx_kgrouped_gemm_mxfp8": ([_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _i32, _vp], ctypes.c_int),
     "mx_blocked_bytes": ([_i64, _i64, _i64], _i64),
     "mx_scales_to_blocked": ([_vp, _i64, _i64, _i64, _vp, _vp], ctypes.c_int),
     "mx_blocked_grouped_bytes": ([_i64, _i64, _i32, _i32], _i64),
@@ -374,6 +375,26 @@ def mx_grouped_gemm_mxfp8(qa, sa, qb, sb, group_end_offsets, out_dtype=torch.bfl
     _check(lib().mx_grouped_gemm_mxfp8(_ptr(qa), _ptr(sa), _ptr(qb), _ptr(sb), _ptr(offs), g, m, n, k, _ptr(c),
                                        int(out_dtype == torch.bfloat16), _stream(qa.device)),
            "mx_grouped_gemm_mxfp8")
+    return c
+
+
+def mx_kgrouped_gemm_mxfp8(qa, sa, qb, sb, group_end_offsets, out_dtype=torch.bfloat16, out=None):
+    """Grouped along K (the weight-gradient GEMM of MoE training): for each
+    group g, C_g = A_g @ B_g^T over the group's K range (its 32-blocks
+    [lo // 32, hi // 32) of the token offsets).  qa (M, K) and qb (N, K) are
+    col-major casts (q_col), sa / sb their scales in the K-grouped blocked
+    layout (as mx_cast_dim0_dim1_grouped_blocked writes s_col_grouped).
+    Returns C (G, M, N)."""
+    m, k = qa.shape
+    n = qb.shape[0]
+    offs = _offsets(group_end_offsets)
+    g = offs.numel()
+    qa, sa = _mx_operand(qa, sa, m, k, mx_blocked_grouped_bytes(m, k // MX_BLOCK, g, 1), "A")
+    qb, sb = _mx_operand(qb, sb, n, k, mx_blocked_grouped_bytes(n, k // MX_BLOCK, g, 1), "B")
+    c = _gemm_out(out, (g, m, n), out_dtype, qa.device)
+    _check(lib().mx_kgrouped_gemm_mxfp8(_ptr(qa), _ptr(sa), _ptr(qb), _ptr(sb), _ptr(offs), g, m, n, k, _ptr(c),
+                                        int(out_dtype == torch.bfloat16), _stream(qa.device)),
+           "mx_kgrouped_gemm_mxfp8")
     return c
 
 

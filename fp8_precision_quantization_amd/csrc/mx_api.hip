@@ -326,9 +326,9 @@ mx_status mx_gemm_mxfp8(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb,
   const mx_status st = check_gemm(qa, sa, qb, sb, m, n, k, c, c_bf16);
   if (st != MX_OK || m == 0 || n == 0)
     return st;
-  if (mx::gemm_grid_blocks(m, n, false, 0) > kMaxGridBlocks)
+  if (mx::gemm_grid_blocks(m, n, 0, 0) > kMaxGridBlocks)
     return MX_ERR_SHAPE;
-  return from_hip(mx::launch_mx_gemm(qa, sa, qb, sb, m, n, k, c, c_bf16 != 0, nullptr, 0, stream));
+  return from_hip(mx::launch_mx_gemm(qa, sa, qb, sb, m, n, k, c, c_bf16 != 0, 0, nullptr, 0, stream));
 }
 
 mx_status mx_grouped_gemm_mxfp8(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, const uint8_t* sb,
@@ -345,10 +345,30 @@ mx_status mx_grouped_gemm_mxfp8(const uint8_t* qa, const uint8_t* sa, const uint
     return MX_ERR_NULL;
   if (!aligned(group_end_offsets, 4))
     return MX_ERR_ALIGN;
-  if (mx::gemm_grid_blocks(m, n, true, num_groups) > kMaxGridBlocks)
+  if (mx::gemm_grid_blocks(m, n, 1, num_groups) > kMaxGridBlocks)
     return MX_ERR_SHAPE;
   return from_hip(
-      mx::launch_mx_gemm(qa, sa, qb, sb, m, n, k, c, c_bf16 != 0, group_end_offsets, num_groups, stream));
+      mx::launch_mx_gemm(qa, sa, qb, sb, m, n, k, c, c_bf16 != 0, 1, group_end_offsets, num_groups, stream));
+}
+
+mx_status mx_kgrouped_gemm_mxfp8(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, const uint8_t* sb,
+                                 const int32_t* group_end_offsets, int32_t num_groups, int64_t m, int64_t n,
+                                 int64_t k, void* c, int32_t c_bf16, hipStream_t stream) {
+  if (num_groups < 1 || num_groups > MX_MAX_GROUPS)
+    return MX_ERR_GROUPS;
+  const mx_status st = check_gemm(qa, sa, qb, sb, m, n, k, c, c_bf16);
+  if (st != MX_OK || m == 0 || n == 0)
+    return st;
+  if (k + 4 * 32 * (int64_t)num_groups >= INT_MAX || m + 128 >= INT_MAX || n + 128 >= INT_MAX)
+    return MX_ERR_SHAPE;
+  if (group_end_offsets == nullptr)
+    return MX_ERR_NULL;
+  if (!aligned(group_end_offsets, 4))
+    return MX_ERR_ALIGN;
+  if (mx::gemm_grid_blocks(m, n, 2, num_groups) > kMaxGridBlocks)
+    return MX_ERR_SHAPE;
+  return from_hip(
+      mx::launch_mx_gemm(qa, sa, qb, sb, m, n, k, c, c_bf16 != 0, 2, group_end_offsets, num_groups, stream));
 }
 
 }  // extern "C"

@@ -235,32 +235,6 @@ struct CastArgs {
   int64_t s1_bytes;
 };
 
-// Column starts of the K-grouped dim1 scales: group g covers scale columns
-// (32-row blocks) [lo_g / 32, hi_g / 32) of the clamped row ranges, padded
-// to a multiple of 4; kstart[g] = sum of the earlier padded widths, kstart[G]
-// the total.  Wave 0 fills it after the row table.
-struct KStarts {
-  int32_t start[MX_MAX_GROUPS + 1];
-};
-struct NoKStarts {};
-
-__device__ inline void build_kstarts(const GroupTable& t, int groups, KStarts& k) {
-  const int lane = threadIdx.x & 63;
-  const int per = (groups + 63) / 64;
-  const int g0 = min(lane * per, groups), g1 = min(g0 + per, groups);
-  int32_t local = 0;
-  for (int g = g0; g < g1; ++g)
-    local += (t.hi[g] / 32 - t.lo[g] / 32 + 3) / 4 * 4;
-  const int32_t incl = wave_incl_sum(local, lane);
-  int32_t run = incl - local;
-  for (int g = g0; g < g1; ++g) {
-    k.start[g] = run;
-    run += (t.hi[g] / 32 - t.lo[g] / 32 + 3) / 4 * 4;
-  }
-  const int32_t total = __shfl(incl, 63);
-  if (lane == 0)
-    k.start[groups] = total;
-}
 
 struct Stage {
   uint4 q1[kTileCols * kSlots];   // dim1 codes, 128 rows x 256 columns

@@ -104,27 +104,68 @@ __device__ __forceinline__ uint16_t to_bf16(float f) {
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
-template <bool GROUPED, bool BF16>
+enum : int { kGemmDense = 0, kGemmGroupsM = 1, kGemmGroupsK = 2 };
+
+template <int MODE, bool BF16>
 __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
+  constexpr bool GROUPED = MODE == kGemmGroupsM;
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kGemmStageBytes];   // [stage][A, B]
 
-  // tile order: XCD x owns ordered tiles [x * per_xcd, (x + 1) * per_xcd)
+  // tile order: XCD x owns ordered tiles [x * per_xcd, (x + 1) * per_xcd);
+  // grouped along K, one grid of tiles per group, group outermost
   const uint32_t tiles = a.tiles_m * a.tiles_n;
-  const uint32_t id = (blockIdx.x % 8) * a.per_xcd + blockIdx.x / 8;
-  if (id >= tiles)
+  uint32_t id = (blockIdx.x % 8) * a.per_xcd + blockIdx.x / 8;
+  if (id >= tiles * (MODE == kGemmGroupsK ? (uint32_t)a.groups : 1u))
     return;  // uniform, before any barrier
+  uint32_t kg = 0;
+  if constexpr (MODE == kGemmGroupsK) {
+    kg = id / tiles;
+    id -= kg * tiles;
+  }
   const uint32_t band = id / (kGemmBand * a.tiles_n);
   const uint32_t band_rows = min((uint32_t)kGemmBand, a.tiles_m - band * kGemmBand);
   const uint32_t within = id - band * kGemmBand * a.tiles_n;
   const uint32_t tm = band * kGemmBand + within % band_rows;
   const uint32_t tn = within / band_rows;
 
-  const int64_t k = a.k;
-  const int64_t kb = k / 32;
+  // k: the reduction length of this tile; ld: the operands' row length
+  int64_t k = a.k;
+  const int64_t ld = a.k;
+  const uint8_t* qa = a.qa;
   const uint8_t* qb = a.qb;
+  const uint8_t* sa = a.sa;
   const uint8_t* sb = a.sb;
+  void* c = a.c;
+  int64_t strip_blocks = (k / 32 + 3) / 4;   // 128 x 4 tiles along a row of the scale layouts
   int64_t row0, rows_valid, srow0;
-  if constexpr (GROUPED) {
+  if constexpr (MODE == kGemmGroupsK) {
+    // Group kg's K range: 32-row (here 32-column) blocks [lo / 32, hi / 32)
+    // of its clamped token range; its scales are its own blocked matrices in
+    // the K-grouped layouts of A and B, at ceil128(rows) * kstart[kg].  The
+    // tables borrow the B half of LDS stage 1 until the first stages load.
+    static_assert(sizeof(GroupTable) + sizeof(KStarts) <= kGemmStageBytes, "group tables fit a stage half");
+    GroupTable& table = *reinterpret_cast<GroupTable*>(lds[1][1]);
+    KStarts& kst = *reinterpret_cast<KStarts*>(lds[1][1] + sizeof(GroupTable));
+    if (threadIdx.x < 64) {
+      build_group_table(a.ends, a.groups, (int32_t)a.k, 32, table);
+      build_kstarts(table, a.groups, kst);
+    }
+    lds_barrier();
+    const int32_t klo = __builtin_amdgcn_readfirstlane(table.lo[kg]) / 32;
+    const int32_t khi = __builtin_amdgcn_readfirstlane(table.hi[kg]) / 32;
+    const int32_t ks = __builtin_amdgcn_readfirstlane(kst.start[kg]);
+    lds_barrier();   // every wave is done with the tables
+    k = 32 * (int64_t)(khi - klo);
+    strip_blocks = (khi - klo + 3) / 4;
+    qa += 32 * (int64_t)klo;
+    qb += 32 * (int64_t)klo;
+    sa += (a.m + 127) / 128 * 128 * (int64_t)ks;
+    sb += (a.n + 127) / 128 * 128 * (int64_t)ks;
+    c = static_cast<uint8_t*>(c) + (int64_t)kg * a.m * a.n * (BF16 ? 2 : 4);
+    row0 = (int64_t)tm * kGemmTile;
+    rows_valid = min((int64_t)kGemmTile, a.m - row0);
+    srow0 = row0;
+  } else if constexpr (GROUPED) {
     // The group table borrows the B half of LDS stage 1 until the first
     // stages are loaded.  (One LDS object keeps the compiler able to tell
     // the loads into one stage from the reads of the other.)
@@ -152,7 +193,7 @@ __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
       part += (table.hi[q] - table.lo[q] + 127) / 128 * 128;
     srow0 = __builtin_amdgcn_readfirstlane(wave_sum(part)) + (r0 - lo);
     lds_barrier();   // every wave is done with the table
-    qb += (int64_t)g * a.n * k;
+    qb += (int64_t)g * a.n * ld;
     sb += (int64_t)g * a.sb_bytes;
   } else {
     row0 = (int64_t)tm * kGemmTile;
@@ -167,16 +208,17 @@ __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
   const int lane = t & 63;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // ranges over the tile's rows of A and of B (rows past them read zero)
-  const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(a.qa + row0 * k, (uint32_t)(rows_valid * k));
-  const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(qb + col0 * k, (uint32_t)(cols_valid * k));
+  // ranges over the tile's rows of A and of B, ending with the last row's
+  // k bytes (rows past them read zero; loads never reach past k in a row)
+  const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(qa + row0 * ld, (uint32_t)((rows_valid - 1) * ld + k));
+  const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(qb + col0 * ld, (uint32_t)((cols_valid - 1) * ld + k));
   // Scales: the wave's 128 rows of A (and of B) are one row of 128 x 4
   // tiles of the blocked layout, a strip of 512 bytes per stage; a wave
   // whose rows all lie past the tile's end reads zero scales.
-  const int64_t strip = (kb + 3) / 4 * 512;
+  const int64_t strip = strip_blocks * 512;
   const bool a_on = rows_valid > wm * 128, b_on = cols_valid > wn * 128;
   const __amdgpu_buffer_rsrc_t rsa =
-      buffer_rsrc(a.sa + (a_on ? (srow0 + wm * 128) / 128 * strip : 0), a_on ? (uint32_t)strip : 0u);
+      buffer_rsrc(sa + (a_on ? (srow0 + wm * 128) / 128 * strip : 0), a_on ? (uint32_t)strip : 0u);
   const __amdgpu_buffer_rsrc_t rsb =
       buffer_rsrc(sb + (b_on ? (col0 + wn * 128) / 128 * strip : 0), b_on ? (uint32_t)strip : 0u);
   // Loader role: load instruction u of wave w fills stage rows 32 u + 8 w ..
@@ -186,7 +228,7 @@ __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
   // row's offset are the same for every u but for 32 u rows.
   const int lrow = 8 * wave + lane / 8;
   const int lchunk = (lane % 8) ^ ((lrow & 7) ^ ((lrow >> 3) & 1));
-  const int g_off = lrow * (int)k + 16 * lchunk;          // + 32 u k (< 2^31 for k <= 2^23)
+  const int g_off = lrow * (int)ld + 16 * lchunk;         // + 32 u ld (< 2^31 for ld <= 2^23)
   // MFMA role
   const int r = lane & 31, h = lane >> 5;
   const int fr = (r & 7) ^ ((r >> 3) & 1);
@@ -211,7 +253,7 @@ __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
     const int row = (u / 2) * kGemmLoadRows + 8 * wave;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(u % 2 ? rb : ra,
                                              (__attribute__((address_space(3))) void*)(lds[st][u % 2] + row * kGemmTK),
-                                             16, off + (u / 2) * kGemmLoadRows * (int)k, kt, 0, 0);
+                                             16, off + (u / 2) * kGemmLoadRows * (int)ld, kt, 0, 0);
   };
   // The stage's scales: lane r + 32 h reads bytes 16 r .. + 15 of the
   // stage's 512-byte tile, whose dword i holds the four block scales of row
@@ -353,16 +395,17 @@ __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
         if (lr < rows_valid) {
           const int64_t idx = (row0 + lr) * a.n + col0 + lc;
           if (BF16)
-            static_cast<uint16_t*>(a.c)[idx] = to_bf16(acc[i][j][v]);
+            static_cast<uint16_t*>(c)[idx] = to_bf16(acc[i][j][v]);
           else
-            static_cast<float*>(a.c)[idx] = acc[i][j][v];
+            static_cast<float*>(c)[idx] = acc[i][j][v];
         }
       }
     }
 }
 
+// mode: kGemmDense, kGemmGroupsM or kGemmGroupsK
 static GemmArgs gemm_args(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, const uint8_t* sb, int64_t m,
-                          int64_t n, int64_t k, void* c, bool grouped, const int32_t* ends, int32_t groups,
+                          int64_t n, int64_t k, void* c, int mode, const int32_t* ends, int32_t groups,
                           int64_t* blocks) {
   GemmArgs a;
   a.qa = qa;
@@ -376,41 +419,45 @@ static GemmArgs gemm_args(const uint8_t* qa, const uint8_t* sa, const uint8_t* q
   a.ends = ends;
   a.groups = groups;
   a.sb_bytes = (n + 127) / 128 * 128 * ((k / 32 + 3) / 4 * 4);
-  // grouped: every group may end with a partial tile -> one spare tile each
-  const int64_t tm = (m + kGemmTile - 1) / kGemmTile + (grouped ? groups : 0);
+  // grouped along M: every group may end with a partial tile -> one spare
+  // tile each; grouped along K: one grid of tiles per group
+  const int64_t tm = (m + kGemmTile - 1) / kGemmTile + (mode == kGemmGroupsM ? groups : 0);
   const int64_t tn = (n + kGemmTile - 1) / kGemmTile;
   a.tiles_m = (uint32_t)tm;
   a.tiles_n = (uint32_t)tn;
-  const int64_t per = (tm * tn + 7) / 8;
+  const int64_t items = tm * tn * (mode == kGemmGroupsK ? groups : 1);
+  const int64_t per = (items + 7) / 8;
   a.per_xcd = (uint32_t)per;
   *blocks = per * 8;
   return a;
 }
 
-int64_t gemm_grid_blocks(int64_t m, int64_t n, bool grouped, int32_t groups) {
+int64_t gemm_grid_blocks(int64_t m, int64_t n, int mode, int32_t groups) {
   int64_t blocks;
-  gemm_args(nullptr, nullptr, nullptr, nullptr, m, n, 64, nullptr, grouped, nullptr, groups, &blocks);
+  gemm_args(nullptr, nullptr, nullptr, nullptr, m, n, 64, nullptr, mode, nullptr, groups, &blocks);
   return blocks;
 }
 
+template <int MODE>
+static void launch_gemm_mode(const GemmArgs& a, bool bf16, dim3 grid, hipStream_t stream) {
+  if (bf16)
+    hipLaunchKernelGGL((mx_gemm_kernel<MODE, true>), grid, dim3(kGemmThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((mx_gemm_kernel<MODE, false>), grid, dim3(kGemmThreads), 0, stream, a);
+}
+
 hipError_t launch_mx_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, const uint8_t* sb, int64_t m,
-                          int64_t n, int64_t k, void* c, bool bf16, const int32_t* ends, int32_t groups,
+                          int64_t n, int64_t k, void* c, bool bf16, int mode, const int32_t* ends, int32_t groups,
                           hipStream_t stream) {
   int64_t blocks;
-  const bool grouped = ends != nullptr;
-  const GemmArgs a = gemm_args(qa, sa, qb, sb, m, n, k, c, grouped, ends, groups, &blocks);
-  const dim3 grid((unsigned)blocks), block(kGemmThreads);
-  if (grouped) {
-    if (bf16)
-      hipLaunchKernelGGL((mx_gemm_kernel<true, true>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((mx_gemm_kernel<true, false>), grid, block, 0, stream, a);
-  } else {
-    if (bf16)
-      hipLaunchKernelGGL((mx_gemm_kernel<false, true>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((mx_gemm_kernel<false, false>), grid, block, 0, stream, a);
-  }
+  const GemmArgs a = gemm_args(qa, sa, qb, sb, m, n, k, c, mode, ends, groups, &blocks);
+  const dim3 grid((unsigned)blocks);
+  if (mode == kGemmGroupsK)
+    launch_gemm_mode<kGemmGroupsK>(a, bf16, grid, stream);
+  else if (mode == kGemmGroupsM)
+    launch_gemm_mode<kGemmGroupsM>(a, bf16, grid, stream);
+  else
+    launch_gemm_mode<kGemmDense>(a, bf16, grid, stream);
   return hipGetLastError();
 }
 

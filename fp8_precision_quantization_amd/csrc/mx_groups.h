@@ -105,4 +105,33 @@ __device__ __forceinline__ int find_source_group(const GroupTable& t, int groups
   return lo;
 }
 
+// Starts of the K-grouped blocked scales of row groups: group g covers scale
+// columns (32-row blocks) [lo_g / 32, hi_g / 32) of its clamped row range,
+// padded to a multiple of 4; kstart[g] = sum of the earlier padded widths,
+// kstart[G] the total.  Wave 0 fills it after the row table (the cast that
+// writes K-grouped column scales, and the GEMM grouped along K that reads
+// them).
+struct KStarts {
+  int32_t start[MX_MAX_GROUPS + 1];
+};
+struct NoKStarts {};
+
+__device__ inline void build_kstarts(const GroupTable& t, int groups, KStarts& k) {
+  const int lane = threadIdx.x & 63;
+  const int per = (groups + 63) / 64;
+  const int g0 = min(lane * per, groups), g1 = min(g0 + per, groups);
+  int32_t local = 0;
+  for (int g = g0; g < g1; ++g)
+    local += (t.hi[g] / 32 - t.lo[g] / 32 + 3) / 4 * 4;
+  const int32_t incl = wave_incl_sum(local, lane);
+  int32_t run = incl - local;
+  for (int g = g0; g < g1; ++g) {
+    k.start[g] = run;
+    run += (t.hi[g] / 32 - t.lo[g] / 32 + 3) / 4 * 4;
+  }
+  const int32_t total = __shfl(incl, 63);
+  if (lane == 0)
+    k.start[groups] = total;
+}
+
 }  // namespace mx

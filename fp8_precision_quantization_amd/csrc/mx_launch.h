@@ -45,10 +45,11 @@ hipError_t launch_tensorwise(const uint16_t* x, int64_t n, uint8_t* q, uint16_t*
 int64_t tensorwise_partials(int64_t n);
 int64_t tensorwise_cast_blocks(int64_t n, bool vec);
 
-// MX-scaled GEMM (grouped along M when ends is non-null); c fp32 or bf16.
+// MX-scaled GEMM, c fp32 or bf16; modes: 0 dense, 1 grouped along M, 2 grouped
+// along K (ends non-null for 1 and 2)
 hipError_t launch_mx_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, const uint8_t* sb, int64_t m,
-                          int64_t n, int64_t k, void* c, bool bf16, const int32_t* ends, int32_t groups,
+                          int64_t n, int64_t k, void* c, bool bf16, int mode, const int32_t* ends, int32_t groups,
                           hipStream_t stream);
-int64_t gemm_grid_blocks(int64_t m, int64_t n, bool grouped, int32_t groups);
+int64_t gemm_grid_blocks(int64_t m, int64_t n, int mode, int32_t groups);
 
 }  // namespace mx

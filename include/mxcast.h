@@ -366,6 +366,30 @@ MX_API mx_status mx_grouped_gemm_mxfp8(const uint8_t* qa, const uint8_t* sa, con
                                        int32_t num_groups, int64_t m, int64_t n, int64_t k, void* c,
                                        int32_t c_bf16, hipStream_t stream);
 
+/*
+ * The same GEMM grouped along K, the weight-gradient GEMM of MoE training:
+ * for each group g, over its range of K (the tokens of expert g),
+ *   C_g[m][n] = sum over k in group g of A(m, k) * B(n, k),
+ * with C_g the g-th of num_groups consecutive (m, n) outputs.  The operands
+ * are the col-major casts of the token-major activations and gradients --
+ * qa (m, k) and qb (n, k) row-major codes as mx_cast_dim0_dim1 writes q_col --
+ * and their scales in the K-grouped blocked layout of the same groups, as
+ * mx_cast_dim0_dim1_grouped_blocked writes s_col_grouped
+ * (mx_blocked_grouped_bytes(m, k / 32, num_groups, 1) bytes for A, likewise
+ * with n for B).
+ *   group_end_offsets  DEVICE int32 [num_groups], cumulative END positions
+ *                      along K (tokens), clamped on the device as by
+ *                      mx_scales_to_blocked_grouped; group g's K range is
+ *                      its 32-blocks [lo_g / 32, hi_g / 32) (the reading of
+ *                      the K-grouped scales); an empty group's C_g is zero.
+ * 1 <= num_groups <= MX_MAX_GROUPS (else MX_ERR_GROUPS), k + 128 *
+ * num_groups < 2^31; other arguments as for mx_gemm_mxfp8.
+ */
+MX_API mx_status mx_kgrouped_gemm_mxfp8(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb,
+                                        const uint8_t* sb, const int32_t* group_end_offsets,
+                                        int32_t num_groups, int64_t m, int64_t n, int64_t k, void* c,
+                                        int32_t c_bf16, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

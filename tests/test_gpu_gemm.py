@@ -208,3 +208,76 @@ def test_gemm_nan_code_and_scale_propagate(oracle_mod, bf16):
     assert np.array_equal(np.isnan(g), nan_want)
     fin = ~nan_want
     _check(got.float()[torch.from_numpy(fin).to(dev)], want[fin], absum[fin], bf16, "finite part")
+
+
+def _kgroup_ref(oracle_mod, qa, sa, qb, sb, ends, k):
+    """Per group, the oracle's GEMM over the group's 32-blocks [lo // 32,
+    hi // 32) of the clamped ends; an empty group gives zeros."""
+    out = []
+    lo = 0
+    for e in ends:
+        hi = min(max(int(e), lo), k)
+        klo, khi = lo // 32, hi // 32
+        if khi > klo:
+            out.append(oracle_mod.mx_gemm(qa[:, 32 * klo:32 * khi], sa[:, klo:khi],
+                                          qb[:, 32 * klo:32 * khi], sb[:, klo:khi]))
+        else:
+            z = np.zeros((qa.shape[0], qb.shape[0]))
+            out.append((z, z))
+        lo = hi
+    return out
+
+
+KGROUP_CASES = [("one", 512, [512]), ("four", 1024, [128, 128, 640, 1024]),
+                ("not_128", 800, [96, 300, 800]),            # 300 -> 9 whole blocks; a K tail per group
+                ("malformed", 640, [300, 200, 900, 640]), ("short", 640, [128, 320]),
+                ("negative", 384, [-40, 100, 384])]
+
+
+@pytest.mark.parametrize("name,k,ends", KGROUP_CASES, ids=[c[0] for c in KGROUP_CASES])
+def test_kgrouped_gemm(oracle_mod, name, k, ends):
+    dev = device()
+    m, n = 200, 136
+    qa, sa = _codes_scales(m, k, 31)
+    qb, sb = _codes_scales(n, k, 32)
+    e = np.asarray(ends, np.int32)
+    sab = to_dev_u8(oracle_mod.to_blocked_grouped(sa, e // 32, 1)[0], dev)
+    sbb = to_dev_u8(oracle_mod.to_blocked_grouped(sb, e // 32, 1)[0], dev)
+    out = torch.full((len(ends), m, n), 12345.0, device=dev)
+    mx.mx_kgrouped_gemm_mxfp8(to_dev_u8(qa, dev), sab, to_dev_u8(qb, dev), sbb, torch.from_numpy(e).to(dev),
+                              out_dtype=torch.float32, out=out)
+    for gi, (want, absum) in enumerate(_kgroup_ref(oracle_mod, qa, sa, qb, sb, ends, k)):
+        _check(out[gi], want, absum, False, "%s group %d" % (name, gi))
+
+
+def test_pipeline_weight_gradient(oracle_mod):
+    """MoE weight gradient: the grouped-blocked casts of the token-major X
+    (T, K) and dY (T, N) feed the K-grouped GEMM dW_g = dY_g^T X_g, against
+    the oracle's dim1 casts and per-group GEMMs."""
+    dev = device()
+    ends = np.array([128, 128, 448, 640], np.int32)
+    x = workloads.heavy_tailed_rows(640, 256, seed=51)
+    dy = workloads.heavy_tailed_rows(640, 192, seed=52)
+    offs = torch.from_numpy(ends).to(dev)
+    _, _, _, qx, sx, _ = mx.mx_cast_dim0_dim1_grouped_blocked(to_dev_bf16(x, dev), offs, raw=True)
+    _, _, _, qdy, sdy, _ = mx.mx_cast_dim0_dim1_grouped_blocked(to_dev_bf16(dy, dev), offs, raw=True)
+    got = mx.mx_kgrouped_gemm_mxfp8(qdy, sdy, qx, sx, offs, out_dtype=torch.float32)
+    oqx, osx = oracle_mod.cast_dim1(x)
+    oqdy, osdy = oracle_mod.cast_dim1(dy)
+    for gi, (want, absum) in enumerate(_kgroup_ref(oracle_mod, oqdy, osdy, oqx, osx, ends, 640)):
+        _check(got[gi], want, absum, False, "weight gradient group %d" % gi)
+
+
+def test_kgrouped_gemm_long_groups(oracle_mod):
+    """The MoE token split (16640 tokens, 4 groups) as K, bf16 out."""
+    dev = device()
+    _, ends = workloads.moe_activations()
+    k = 16640
+    m, n = 256, 320
+    qa, sa = _codes_scales(m, k, 61)
+    qb, sb = _codes_scales(n, k, 62)
+    sab = to_dev_u8(oracle_mod.to_blocked_grouped(sa, ends // 32, 1)[0], dev)
+    sbb = to_dev_u8(oracle_mod.to_blocked_grouped(sb, ends // 32, 1)[0], dev)
+    got = mx.mx_kgrouped_gemm_mxfp8(to_dev_u8(qa, dev), sab, to_dev_u8(qb, dev), sbb, torch.from_numpy(ends).to(dev))
+    for gi, (want, absum) in enumerate(_kgroup_ref(oracle_mod, qa, sa, qb, sb, ends, k)):
+        _check(got[gi], want, absum, True, "long group %d" % gi)

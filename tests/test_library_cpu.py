@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
                           "mx_cast_dim0_dim1_mgrouped", "mx_cast_dim0_dim1_grouped_blocked",
                           "mx_cast_dim1_3d", "mx_cast_dim1_3d_blocked", "mx_quantize_fp8_rowwise",
                           "mx_tensorwise_workspace_bytes", "mx_quantize_fp8_tensorwise",
-                          "mx_gemm_mxfp8", "mx_grouped_gemm_mxfp8",
+                          "mx_gemm_mxfp8", "mx_grouped_gemm_mxfp8", "mx_kgrouped_gemm_mxfp8",
                           "mx_blocked_bytes", "mx_scales_to_blocked",
                           "mx_blocked_grouped_bytes", "mx_scales_to_blocked_grouped"}
     for n in names:
@@ -147,6 +147,12 @@ def test_gemm_validation(lib):
     assert g(P, P, P, P, ctypes.c_void_p(0x10002), 2, 64, 64, 64, P, 1, None) == ERR_ALIGN
     assert g(P, P, P, P, P, 2, (1 << 31) - 200, 64, 64, P, 1, None) == ERR_SHAPE
     assert g(P, P, P, P, P, 2, (1 << 31) - 300, 64, 64, P, 1, None) == ERR_SHAPE   # m + 256 G
+    h = lib.mx_kgrouped_gemm_mxfp8
+    assert h(P, P, P, P, P, 0, 64, 64, 64, P, 1, None) == ERR_GROUPS
+    assert h(P, P, P, P, None, 2, 64, 64, 64, P, 1, None) == ERR_NULL
+    assert h(P, P, P, P, ctypes.c_void_p(0x10002), 2, 64, 64, 64, P, 1, None) == ERR_ALIGN
+    assert h(P, P, P, P, P, 2, 64, 64, 48, P, 1, None) == ERR_SHAPE               # k % 32
+    assert h(P, ctypes.c_void_p(0x10008), P, P, P, 2, 64, 64, 64, P, 1, None) == ERR_ALIGN
 
 
 def test_rowwise_validation(lib):
