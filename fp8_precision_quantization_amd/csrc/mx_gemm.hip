@@ -111,16 +111,17 @@ __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
   constexpr bool GROUPED = MODE == kGemmGroupsM;
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kGemmStageBytes];   // [stage][A, B]
 
-  // tile order: XCD x owns ordered tiles [x * per_xcd, (x + 1) * per_xcd);
-  // grouped along K, one grid of tiles per group, group outermost
+  // tile order: XCD x owns ordered tiles [x * per_xcd, (x + 1) * per_xcd).
+  // Grouped along K, one grid of tiles per group, the group innermost: the
+  // groups' K lengths differ, and so every XCD gets the same mix of them.
   const uint32_t tiles = a.tiles_m * a.tiles_n;
   uint32_t id = (blockIdx.x % 8) * a.per_xcd + blockIdx.x / 8;
   if (id >= tiles * (MODE == kGemmGroupsK ? (uint32_t)a.groups : 1u))
     return;  // uniform, before any barrier
   uint32_t kg = 0;
   if constexpr (MODE == kGemmGroupsK) {
-    kg = id / tiles;
-    id -= kg * tiles;
+    kg = id % (uint32_t)a.groups;
+    id /= (uint32_t)a.groups;
   }
   const uint32_t band = id / (kGemmBand * a.tiles_n);
   const uint32_t band_rows = min((uint32_t)kGemmBand, a.tiles_m - band * kGemmBand);
