@@ -69,6 +69,7 @@ constexpr int kGemmLoadRows = kGemmThreads * 16 / kGemmTK;   // rows per load in
 constexpr int kGemmLoads = kGemmTile / kGemmLoadRows;        // load instructions per operand and stage (8)
 constexpr int kGemmStageBytes = kGemmTile * kGemmTK;         // one operand's stage (32 KiB)
 constexpr int kGemmBand = 8;                   // tile rows per band of the tile order
+constexpr int kGemmOrderMax = 64;              // grouped along K: groups ordered by K length up to this count
 
 struct GemmArgs {
   const uint8_t *qa, *sa, *qb, *sb;
@@ -112,17 +113,22 @@ __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kGemmStageBytes];   // [stage][A, B]
 
   // tile order: XCD x owns ordered tiles [x * per_xcd, (x + 1) * per_xcd).
-  // Grouped along K, one grid of tiles per group, the group innermost: the
-  // groups' K lengths differ, and so every XCD gets the same mix of them.
+  // Grouped along K there is one grid of tiles per group and each group's
+  // ordered tiles are cut into 8 pieces of per_xcd, one per XCD; an XCD
+  // runs its piece of every group, one group after the other, the group
+  // with the longest K range first (the groups' K lengths differ widely,
+  // and short tiles last keep the CUs' finishing times close together).
   const uint32_t tiles = a.tiles_m * a.tiles_n;
   uint32_t id = (blockIdx.x % 8) * a.per_xcd + blockIdx.x / 8;
-  if (id >= tiles * (MODE == kGemmGroupsK ? (uint32_t)a.groups : 1u))
-    return;  // uniform, before any barrier
-  uint32_t kg = 0;
+  uint32_t kslot = 0;   // grouped along K: this tile's place in the group order
   if constexpr (MODE == kGemmGroupsK) {
-    kg = id % (uint32_t)a.groups;
-    id /= (uint32_t)a.groups;
+    kslot = (blockIdx.x / 8) / a.per_xcd;
+    id = (blockIdx.x % 8) * a.per_xcd + (blockIdx.x / 8) % a.per_xcd;
+    if (kslot >= (uint32_t)a.groups)
+      return;  // uniform, before any barrier
   }
+  if (id >= tiles)
+    return;  // uniform, before any barrier
   const uint32_t band = id / (kGemmBand * a.tiles_n);
   const uint32_t band_rows = min((uint32_t)kGemmBand, a.tiles_m - band * kGemmBand);
   const uint32_t within = id - band * kGemmBand * a.tiles_n;
@@ -139,27 +145,49 @@ __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
   void* c = a.c;
   int64_t strip_blocks = (k / 32 + 3) / 4;   // 128 x 4 tiles along a row of the scale layouts
   int64_t row0, rows_valid, srow0;
+  // Grouped along K, stages stay on 128-byte boundaries of the operand rows
+  // (a stage that straddles two cache lines per row costs about a third
+  // more): the group's first stage starts kofs = 32 d bytes before its first
+  // block, d = (first block) % 4, and its chunks outside the group load zero.
+  int kofs = 0;
   if constexpr (MODE == kGemmGroupsK) {
     // Group kg's K range: 32-row (here 32-column) blocks [lo / 32, hi / 32)
     // of its clamped token range; its scales are its own blocked matrices in
     // the K-grouped layouts of A and B, at ceil128(rows) * kstart[kg].  The
     // tables borrow the B half of LDS stage 1 until the first stages load.
-    static_assert(sizeof(GroupTable) + sizeof(KStarts) <= kGemmStageBytes, "group tables fit a stage half");
+    static_assert(sizeof(GroupTable) + sizeof(KStarts) + kGemmOrderMax * sizeof(int32_t) <= kGemmStageBytes,
+                  "group tables fit a stage half");
     GroupTable& table = *reinterpret_cast<GroupTable*>(lds[1][1]);
     KStarts& kst = *reinterpret_cast<KStarts*>(lds[1][1] + sizeof(GroupTable));
+    int32_t* order = reinterpret_cast<int32_t*>(lds[1][1] + sizeof(GroupTable) + sizeof(KStarts));
     if (threadIdx.x < 64) {
       build_group_table(a.ends, a.groups, (int32_t)a.k, 32, table);
       build_kstarts(table, a.groups, kst);
+      // up to 64 groups: longest block count first, ties by index (lane g
+      // counts the groups that go before it)
+      if (a.groups <= kGemmOrderMax) {
+        const int g = threadIdx.x;
+        const int32_t len = g < a.groups ? table.hi[g] / 32 - table.lo[g] / 32 : -1;
+        int rank = 0;
+        for (int q = 0; q < a.groups; ++q) {
+          const int32_t lq = __shfl(len, q);
+          rank += (lq > len) || (lq == len && q < g);
+        }
+        if (g < a.groups)
+          order[rank] = g;
+      }
     }
     lds_barrier();
+    const int kg = a.groups <= kGemmOrderMax ? __builtin_amdgcn_readfirstlane(order[kslot]) : (int)kslot;
     const int32_t klo = __builtin_amdgcn_readfirstlane(table.lo[kg]) / 32;
     const int32_t khi = __builtin_amdgcn_readfirstlane(table.hi[kg]) / 32;
     const int32_t ks = __builtin_amdgcn_readfirstlane(kst.start[kg]);
     lds_barrier();   // every wave is done with the tables
     k = 32 * (int64_t)(khi - klo);
     strip_blocks = (khi - klo + 3) / 4;
-    qa += 32 * (int64_t)klo;
-    qb += 32 * (int64_t)klo;
+    kofs = 32 * (klo % 4);
+    qa += 32 * (int64_t)klo - kofs;
+    qb += 32 * (int64_t)klo - kofs;
     sa += (a.m + 127) / 128 * 128 * (int64_t)ks;
     sb += (a.n + 127) / 128 * 128 * (int64_t)ks;
     c = static_cast<uint8_t*>(c) + (int64_t)kg * a.m * a.n * (BF16 ? 2 : 4);
@@ -211,8 +239,8 @@ __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
 
   // ranges over the tile's rows of A and of B, ending with the last row's
   // k bytes (rows past them read zero; loads never reach past k in a row)
-  const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(qa + row0 * ld, (uint32_t)((rows_valid - 1) * ld + k));
-  const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(qb + col0 * ld, (uint32_t)((cols_valid - 1) * ld + k));
+  const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(qa + row0 * ld, (uint32_t)((rows_valid - 1) * ld + kofs + k));
+  const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(qb + col0 * ld, (uint32_t)((cols_valid - 1) * ld + kofs + k));
   // Scales: the wave's 128 rows of A (and of B) are one row of 128 x 4
   // tiles of the blocked layout, a strip of 512 bytes per stage; a wave
   // whose rows all lie past the tile's end reads zero scales.
@@ -242,15 +270,20 @@ __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
     for (int j = 0; j < kGemmWaveBlocks; ++j)
       acc[i][j] = (v16f){};
 
-  const int stages = (int)((k + kGemmTK - 1) / kGemmTK);
-  uint32_t s0a[kGemmWaveBlocks], s0b[kGemmWaveBlocks], s1a[kGemmWaveBlocks], s1b[kGemmWaveBlocks];
+  const int stages = (int)((kofs + k + kGemmTK - 1) / kGemmTK);
+  // a stage's scale words per operand: the stage's tile, and grouped along
+  // K also the tile before it (combined when the scales are used, so that
+  // no wait for the scale loads stands before the MFMAs that follow them)
+  constexpr int kSW = MODE == kGemmGroupsK ? 2 * kGemmWaveBlocks : kGemmWaveBlocks;
+  uint32_t s0a[kSW], s0b[kSW], s1a[kSW], s1b[kSW];
 
   // Load u (0 .. 15) of a stage: load instruction u / 2 of operand u % 2,
-  // from memory straight into LDS half st.  Chunks past K (all of them when
-  // kt >= K) get an offset past the buffer's range and load zero.
+  // from memory straight into LDS half st.  Chunks outside [kofs, kofs + K)
+  // (all of them when kt >= kofs + K) get an offset past the buffer's range
+  // and load zero.
   auto load_one = [&](auto st_c, int kt, int u) {
     constexpr int st = decltype(st_c)::value;
-    const int off = kt + 16 * lchunk < k ? g_off : (int)0x80000000;
+    const int off = (uint32_t)(kt + 16 * lchunk - kofs) < (uint32_t)k ? g_off : (int)0x80000000;
     const int row = (u / 2) * kGemmLoadRows + 8 * wave;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(u % 2 ? rb : ra,
                                              (__attribute__((address_space(3))) void*)(lds[st][u % 2] + row * kGemmTK),
@@ -259,14 +292,28 @@ __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
   // The stage's scales: lane r + 32 h reads bytes 16 r .. + 15 of the
   // stage's 512-byte tile, whose dword i holds the four block scales of row
   // 32 i + r.  Blocks past K are the layout's zero padding (their data is
-  // zero too); a stage past K reads zero.
-  auto load_scales = [&](int kt, uint32_t (&s_a)[kGemmWaveBlocks], uint32_t (&s_b)[kGemmWaveBlocks]) {
+  // zero too); a stage past K reads zero.  With kofs = 32 d the stage's
+  // blocks are the group's blocks 4 j - d .. 4 j - d + 3: the last d bytes
+  // of tile j - 1 and the first 4 - d of tile j (blocks before the group's
+  // first, tile -1, read zero, as their data does).
+  auto load_scales = [&](int kt, uint32_t (&s_a)[kSW], uint32_t (&s_b)[kSW]) {
     const u32x4 va = __builtin_amdgcn_raw_buffer_load_b128(rsa, 16 * r, kt / kGemmTK * 512, 0);
     const u32x4 vb = __builtin_amdgcn_raw_buffer_load_b128(rsb, 16 * r, kt / kGemmTK * 512, 0);
 #pragma unroll
     for (int i = 0; i < kGemmWaveBlocks; ++i) {
       s_a[i] = va[i];
       s_b[i] = vb[i];
+    }
+    if constexpr (MODE == kGemmGroupsK) {
+      // (with d = 0 none of its bytes is used: it loads zero, from no memory)
+      const int poff = kt >= kGemmTK && kofs != 0 ? 16 * r + (kt / kGemmTK - 1) * 512 : (int)0x80000000;
+      const u32x4 pa = __builtin_amdgcn_raw_buffer_load_b128(rsa, poff, 0, 0);
+      const u32x4 pb = __builtin_amdgcn_raw_buffer_load_b128(rsb, poff, 0, 0);
+#pragma unroll
+      for (int i = 0; i < kGemmWaveBlocks; ++i) {
+        s_a[kGemmWaveBlocks + i] = pa[i];
+        s_b[kGemmWaveBlocks + i] = pb[i];
+      }
     }
   };
   // MFMA operands of one step as 16-byte halves: [slab][0] = chunk 4 s + h
@@ -291,11 +338,19 @@ __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
                          (int)fb[j][1][0], (int)fb[j][1][1], (int)fb[j][1][2], (int)fb[j][1][3]};
     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, vb, acc[i][j], 0, 0, 0, xa, 0, xb);
   };
-  // this lane's scale bytes for step s: stage block 2 s + h
-  auto step_scales = [&](int s, const uint32_t (&sc)[kGemmWaveBlocks], int (&x)[kGemmWaveBlocks]) {
+  // this lane's scale bytes for step s: stage block 2 s + h (grouped along
+  // K: byte 2 s + h of the last d bytes of the previous tile followed by the
+  // first 4 - d of the stage's tile)
+  auto step_scales = [&](int s, const uint32_t (&sc)[kSW], int (&x)[kGemmWaveBlocks]) {
 #pragma unroll
-    for (int i = 0; i < kGemmWaveBlocks; ++i)
-      x[i] = (int)((sc[i] >> (16 * s + 8 * h)) & 0xFFu);
+    for (int i = 0; i < kGemmWaveBlocks; ++i) {
+      if constexpr (MODE == kGemmGroupsK) {
+        const uint64_t pair = ((uint64_t)sc[i] << 32) | sc[kGemmWaveBlocks + i];
+        x[i] = (int)((pair >> (32 - 8 * (kofs / 32) + 16 * s + 8 * h)) & 0xFFu);
+      } else {
+        x[i] = (int)((sc[i] >> (16 * s + 8 * h)) & 0xFFu);
+      }
+    }
   };
 
   // Stage t (LDS half st = t % 2, K offset kt) runs in two halves.
@@ -311,8 +366,8 @@ __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
   // last MFMA of a stage and the first of the next.  Stages past K load
   // zero.  sched_barrier keeps the compiler to this instruction order.
   auto first_half = [&](auto st_c, int kt, const Half& f0a, const Half& f0b,
-                        const uint32_t (&cur_a)[kGemmWaveBlocks], const uint32_t (&cur_b)[kGemmWaveBlocks],
-                        uint32_t (&nxt_a)[kGemmWaveBlocks], uint32_t (&nxt_b)[kGemmWaveBlocks], Half& f1a,
+                        const uint32_t (&cur_a)[kSW], const uint32_t (&cur_b)[kSW],
+                        uint32_t (&nxt_a)[kSW], uint32_t (&nxt_b)[kSW], Half& f1a,
                         Half& f1b) {
     load_scales(kt + kGemmTK, nxt_a, nxt_b);
     int xa[kGemmWaveBlocks], xb[kGemmWaveBlocks];
@@ -327,16 +382,16 @@ __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
     }
   };
   auto second_half = [&](auto st_c, int kt, const Half& f1a, const Half& f1b,
-                         const uint32_t (&cur_a)[kGemmWaveBlocks], const uint32_t (&cur_b)[kGemmWaveBlocks],
+                         const uint32_t (&cur_a)[kSW], const uint32_t (&cur_b)[kSW],
                          Half& f0a, Half& f0b) {
     constexpr int st = decltype(st_c)::value;
     int xa[kGemmWaveBlocks], xb[kGemmWaveBlocks];
     step_scales(1, cur_a, xa);
     step_scales(1, cur_b, xb);
     __builtin_amdgcn_sched_barrier(0);
-    // all but the scale loads of stage t + 1: this wave's loads of stage
-    // t + 1 (vmcnt), then every wave's
-    __builtin_amdgcn_s_waitcnt(0x0F70 | 2);
+    // all but the scale loads of stage t + 1 (two, or four grouped along
+    // K): this wave's loads of stage t + 1 (vmcnt), then every wave's
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (MODE == kGemmGroupsK ? 4 : 2));
     lds_barrier();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -421,15 +476,15 @@ static GemmArgs gemm_args(const uint8_t* qa, const uint8_t* sa, const uint8_t* q
   a.groups = groups;
   a.sb_bytes = (n + 127) / 128 * 128 * ((k / 32 + 3) / 4 * 4);
   // grouped along M: every group may end with a partial tile -> one spare
-  // tile each; grouped along K: one grid of tiles per group
+  // tile each; grouped along K: one grid of tiles per group, each cut into
+  // 8 pieces of per_xcd tiles, one per XCD
   const int64_t tm = (m + kGemmTile - 1) / kGemmTile + (mode == kGemmGroupsM ? groups : 0);
   const int64_t tn = (n + kGemmTile - 1) / kGemmTile;
   a.tiles_m = (uint32_t)tm;
   a.tiles_n = (uint32_t)tn;
-  const int64_t items = tm * tn * (mode == kGemmGroupsK ? groups : 1);
-  const int64_t per = (items + 7) / 8;
+  const int64_t per = (tm * tn + 7) / 8;
   a.per_xcd = (uint32_t)per;
-  *blocks = per * 8;
+  *blocks = per * 8 * (mode == kGemmGroupsK ? groups : 1);
   return a;
 }
 

@@ -231,7 +231,9 @@ def _kgroup_ref(oracle_mod, qa, sa, qb, sb, ends, k):
 KGROUP_CASES = [("one", 512, [512]), ("four", 1024, [128, 128, 640, 1024]),
                 ("not_128", 800, [96, 300, 800]),            # 300 -> 9 whole blocks; a K tail per group
                 ("malformed", 640, [300, 200, 900, 640]), ("short", 640, [128, 320]),
-                ("negative", 384, [-40, 100, 384])]
+                ("negative", 384, [-40, 100, 384]),
+                ("ties", 1024, [256, 512, 768, 1024]),                # equal K lengths: kept in index order
+                ("many", 4224, [60 * i for i in range(1, 70)] + [4224])]   # 70 groups: past the ordered count
 
 
 @pytest.mark.parametrize("name,k,ends", KGROUP_CASES, ids=[c[0] for c in KGROUP_CASES])
