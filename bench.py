@@ -227,6 +227,27 @@ def c_call(name, *args):
     return call
 
 
+def oracle_leg(nbytes, sample, run, compare):
+    """The CPU oracle timed on the host's cores: run() computes the oracle's
+    outputs (timed), compare(result) returns {name: mismatched bytes} against
+    the GPU's outputs (not timed)."""
+    import oracle
+    t0 = time.perf_counter()
+    res = run(oracle)
+    dt = time.perf_counter() - t0
+    bad = compare(res)
+    ok = not any(bad.values())
+    return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "sample": "%s, %.1f s wall" % (sample, dt), "matches_gpu": bool(ok),
+            **({} if ok else {"mismatched_bytes": bad})}
+
+
+def n_bad(gpu, ref):
+    g = gpu.cpu().numpy().reshape(-1)
+    r = np.asarray(ref).reshape(-1)
+    return int(np.count_nonzero(g != r)) if g.shape == r.shape else -1
+
+
 # --------------------------------------------------------------------------
 # workloads
 # --------------------------------------------------------------------------
@@ -359,8 +380,22 @@ def setup_moe(dev, fused=True):
         nb = cast_bytes(rows, cols) + rows * (cols // 32) + out.numel()
         name = "cast dim0+dim1"
         label = "mx_cast_dim0_dim1 %dx%d bf16 + M-grouped blocked layout (%d groups)"
+
+    def cpu_baseline():
+        def run(o):
+            r_q0, r_s0 = o.cast_dim0(bits)
+            r_q1, r_s1 = o.cast_dim1(bits)
+            return r_q0, r_q1, r_s1, o.to_blocked_grouped(r_s0, ends, 0)
+
+        def compare(r):
+            r_q0, r_q1, r_s1, (r_g, r_st) = r
+            return {"q_row": n_bad(q0, r_q0), "q_col": n_bad(q1, r_q1), "s_col": n_bad(s1, r_s1),
+                    "s_row_mgrouped": n_bad(out, r_g), "starts": n_bad(starts, r_st)}
+        return oracle_leg(nb, "the whole %dx%d input (dim0+dim1 cast, M-grouped blocked row scales)"
+                          % (rows, cols), run, compare)
+
     config = {"workload": label % (rows, cols, g), "rows": rows, "cols": cols, "groups": g}
-    return step, nb, timer, kb, name, None, config
+    return step, nb, timer, kb, name, cpu_baseline, config
 
 
 def setup_moe_2launch(dev):
@@ -414,8 +449,23 @@ def setup_moe_both(dev, fused=True):
         nb = kb + s1.numel() + s1g.numel()
         name = "cast dim0+dim1, M-grouped row scales"
         label = "mx_cast_dim0_dim1_mgrouped %dx%d bf16 + K-grouped layout of the column scales (%d groups)"
+
+    def cpu_baseline():
+        def run(o):
+            r_q0, r_s0 = o.cast_dim0(bits)
+            r_q1, r_s1 = o.cast_dim1(bits)
+            return r_q0, r_q1, o.to_blocked_grouped(r_s0, ends, 0), o.to_blocked_grouped(r_s1, ends // 32, 1)
+
+        def compare(r):
+            r_q0, r_q1, (r_g0, r_rs), (r_g1, r_cs) = r
+            return {"q_row": n_bad(q0, r_q0), "q_col": n_bad(q1, r_q1), "s_row_mgrouped": n_bad(s0g, r_g0),
+                    "s_col_kgrouped": n_bad(s1g, r_g1), "row_starts": n_bad(rs, r_rs),
+                    "col_starts": n_bad(cs, r_cs)}
+        return oracle_leg(nb, "the whole %dx%d input (dim0+dim1 cast, M-grouped row and K-grouped column "
+                          "scales)" % (rows, cols), run, compare)
+
     config = {"workload": label % (rows, cols, g), "rows": rows, "cols": cols, "groups": g}
-    return step, nb, timer, kb, name, None, config
+    return step, nb, timer, kb, name, cpu_baseline, config
 
 
 def setup_moe_both_2launch(dev):
@@ -449,9 +499,23 @@ def setup_kgroups(dev):
 
     nb = sum(s.numel() + out.numel() for s, _, out, _ in items)
     big = items[1][0].numel() + items[1][2].numel()
+
+    def cpu_baseline():
+        host = [(s.cpu().numpy(), offs.cpu().numpy()) for s, offs, _, _ in items]
+
+        def run(o):
+            return [o.to_blocked_grouped(s, e, 1) for s, e in host]
+
+        def compare(r):
+            bad = {}
+            for (_, _, out, starts), (r_out, r_st), shape in zip(items, r, workloads.K_GROUP_SHAPES):
+                bad["%dx%d" % shape] = n_bad(out, r_out) + n_bad(starts, r_st)
+            return bad
+        return oracle_leg(nb, "all three scale tensors", run, compare)
+
     config = {"workload": "K-grouped blocked layout of e8m0 scales %s, 4 groups each"
                           % (list(workloads.K_GROUP_SHAPES),)}
-    return step, nb, timer, big, "K-grouped layout (8192, 4096)", None, config
+    return step, nb, timer, big, "K-grouped layout (8192, 4096)", cpu_baseline, config
 
 
 def setup_experts(dev, experts=16, n=8192, k=5120, fused=True):
@@ -489,11 +553,28 @@ def setup_experts(dev, experts=16, n=8192, k=5120, fused=True):
         cb = experts * n * k * 3 + experts * n * k // 32
         nb = cb + blocked_bytes(k, n // 32, experts)
         name = "cast dim1 3D"
+
+    def cpu_baseline(sample=2):
+        # a bounded sample: the first two experts (of the same workload)
+        host = [workloads.expert_weight(e, n, k) for e in range(sample)]
+
+        def run(o):
+            outs = []
+            for we in host:
+                r_q, r_s = o.cast_dim1(we)
+                outs.append((r_q, o.to_blocked(r_s)))
+            return outs
+
+        def compare(r):
+            return {"expert %d" % e: n_bad(q[e], r_q) + n_bad(out[e], r_b) for e, (r_q, r_b) in enumerate(r)}
+        per_expert = nb // experts
+        return oracle_leg(per_expert * sample, "the first %d of the %d experts (dim1 cast and blocked scales of "
+                          "each (%d, %d) expert)" % (sample, experts, n, k), run, compare)
     config = {"workload": "%s (%d, %d, %d) bf16 + per-expert blocked scale layout%s"
                           % ("mx_cast_dim1_3d_blocked" if fused else "mx_cast_dim1_3d", experts, n, k,
                              "" if fused else " by mx_scales_to_blocked"),
               "experts": experts, "n": n, "k": k}
-    return step, nb, timer, cb, name, None, config
+    return step, nb, timer, cb, name, cpu_baseline, config
 
 
 def setup_experts_2launch(dev):
