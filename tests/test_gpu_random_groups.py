@@ -1,0 +1,105 @@
+"""Seeded random group splits on the GPU: shapes and cumulative end offsets
+drawn from a seed (empty groups, unsorted and out-of-range ends included),
+for the grouped casts, the grouped layouts and the GEMM grouped along K, each
+against the oracle.  The fixed cases in the other files cover the layouts'
+corners by construction; these add splits nobody chose by hand."""
+import numpy as np
+import pytest
+import torch
+
+import fp8_precision_quantization_amd as mx
+from fp8_precision_quantization_amd import workloads
+from tests import test_gpu_gemm as gemm_t
+from tests import test_gpu_grouped_blocked as gb_t
+from tests import test_gpu_mgrouped as mg_t
+from tests.gpu_util import assert_bytes_equal, device, host, sentinel, to_dev_u8
+
+pytestmark = pytest.mark.gpu
+
+SEEDS = list(range(8))
+
+
+def _ends(rng, extent, unit):
+    """G in 1..9 cumulative ends, multiples of `unit` mostly; now and then an
+    end off the unit grid, a repeated end (an empty group), a decreasing or a
+    negative end, or a last end short of / past the extent."""
+    g = int(rng.integers(1, 10))
+    ends = np.sort(rng.integers(0, extent // unit + 1, size=g)) * unit
+    if g > 1 and rng.random() < 0.3:
+        ends[int(rng.integers(0, g - 1))] += int(rng.integers(1, unit))   # off the grid
+    if g > 2 and rng.random() < 0.2:
+        i = int(rng.integers(1, g))
+        ends[i] = ends[i - 1] - unit                                     # decreasing
+    if rng.random() < 0.1:
+        ends[0] = -int(rng.integers(1, 100))                             # negative
+    r = rng.random()
+    if r < 0.6:
+        ends[-1] = extent
+    elif r < 0.8:
+        ends[-1] = extent + unit                                         # past the extent
+    return [int(e) for e in ends]
+
+
+def _shape(rng, max_rows=40, max_cols=40):
+    return 32 * int(rng.integers(1, max_rows + 1)), 32 * int(rng.integers(1, max_cols + 1))
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_grouped_blocked_cast(oracle_mod, seed):
+    rng = np.random.default_rng([401, seed])
+    shape = _shape(rng)
+    ends = _ends(rng, shape[0], 32)
+    bits = workloads.normal_bf16(shape, seed=[402, seed])
+    gb_t.check(oracle_mod, bits, ends, device(), "seed %d %s ends %s" % (seed, shape, ends))
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_mgrouped_cast(oracle_mod, seed):
+    rng = np.random.default_rng([403, seed])
+    shape = _shape(rng)
+    ends = _ends(rng, shape[0], 32)
+    bits = workloads.heavy_tailed_rows(shape[0], shape[1], seed=404 + seed)
+    mg_t.check(oracle_mod, bits, ends, device(), "seed %d %s ends %s" % (seed, shape, ends))
+
+
+@pytest.mark.parametrize("axis", [0, 1])
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_grouped_layout(oracle_mod, seed, axis):
+    dev = device()
+    rng = np.random.default_rng([405, seed, axis])
+    r, c = int(rng.integers(1, 700)), int(rng.integers(1, 90))
+    s = rng.integers(0, 256, size=(r, c), dtype=np.uint8)
+    ends = np.asarray(_ends(rng, r if axis == 0 else c, 32 if axis == 0 else 4), np.int32)
+    g = len(ends)
+    shape = (r + 128 * g, -(-c // 4) * 4) if axis == 0 else (-(-r // 128) * 128, -(-c // 4) * 4 + 4 * g)
+    assert shape[0] * shape[1] == mx.mx_blocked_grouped_bytes(r, c, g, axis)
+    out = sentinel(shape, dev)
+    starts = torch.full((g + 1,), -7, dtype=torch.int64, device=dev)
+    mx.mx_scales_to_blocked_grouped(to_dev_u8(s, dev), torch.from_numpy(ends).to(dev), axis, out=out,
+                                    out_group_starts=starts, raw=True)
+    torch.cuda.synchronize(dev)
+    r_out, r_starts = oracle_mod.to_blocked_grouped(s, ends, axis)
+    what = "seed %d axis %d (%d, %d) ends %s" % (seed, axis, r, c, ends.tolist())
+    assert_bytes_equal(host(out).reshape(-1), r_out, what + " layout")
+    assert_bytes_equal(host(starts), r_starts, what + " starts")
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_kgrouped_gemm(oracle_mod, seed):
+    dev = device()
+    rng = np.random.default_rng([407, seed])
+    m, n = int(rng.integers(1, 300)), int(rng.integers(1, 300))
+    k = 32 * int(rng.integers(1, 48))
+    ends = _ends(rng, k, 32)
+    qa, sa = gemm_t._codes_scales(m, k, [408, seed])
+    qb, sb = gemm_t._codes_scales(n, k, [409, seed])
+    e = np.asarray(ends, np.int32)
+    # token offsets clamped as the kernel clamps them, then counted in blocks
+    sab = to_dev_u8(oracle_mod.to_blocked_grouped(sa, e // 32, 1)[0], dev)
+    sbb = to_dev_u8(oracle_mod.to_blocked_grouped(sb, e // 32, 1)[0], dev)
+    out = torch.full((len(ends), m, n), 12345.0, device=dev)
+    mx.mx_kgrouped_gemm_mxfp8(to_dev_u8(qa, dev), sab, to_dev_u8(qb, dev), sbb, torch.from_numpy(e).to(dev),
+                              out_dtype=torch.float32, out=out)
+    for gi, (want, absum) in enumerate(gemm_t._kgroup_ref(oracle_mod, qa, sa, qb, sb, ends, k)):
+        gemm_t._check(out[gi], want, absum, False, "seed %d (%d, %d, %d) ends %s group %d"
+                      % (seed, m, n, k, ends, gi))
