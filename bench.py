@@ -242,6 +242,28 @@ def oracle_leg(nbytes, sample, run, compare):
             **({} if ok else {"mismatched_bytes": bad})}
 
 
+def moe_single_thread(bits, ends, sample_rows=1024):
+    """One thread of the oracle on the first 1024 rows of the MoE input (the
+    same cast and M-grouped layout, the groups cut at the sample's end)."""
+    import oracle
+    cores = oracle.num_threads()
+    part = np.ascontiguousarray(bits[:sample_rows])
+    e = np.minimum(ends, sample_rows).astype(np.int32)
+    r, c = part.shape
+    oracle.set_num_threads(1)
+    try:
+        t0 = time.perf_counter()
+        _, s0 = oracle.cast_dim0(part)
+        oracle.cast_dim1(part)
+        g, _ = oracle.to_blocked_grouped(s0, e, 0)
+        dt = time.perf_counter() - t0
+    finally:
+        oracle.set_num_threads(cores)
+    nbytes = r * c * 4 + r * (c // 32) + g.size
+    return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s",
+            "sample": "the first %d rows, one thread, %.2f s" % (sample_rows, dt)}
+
+
 def n_bad(gpu, ref):
     g = gpu.cpu().numpy().reshape(-1)
     r = np.asarray(ref).reshape(-1)
@@ -391,8 +413,10 @@ def setup_moe(dev, fused=True):
             r_q0, r_q1, r_s1, (r_g, r_st) = r
             return {"q_row": n_bad(q0, r_q0), "q_col": n_bad(q1, r_q1), "s_col": n_bad(s1, r_s1),
                     "s_row_mgrouped": n_bad(out, r_g), "starts": n_bad(starts, r_st)}
-        return oracle_leg(nb, "the whole %dx%d input (dim0+dim1 cast, M-grouped blocked row scales)"
-                          % (rows, cols), run, compare)
+        leg = oracle_leg(nb, "the whole %dx%d input (dim0+dim1 cast, M-grouped blocked row scales)"
+                         % (rows, cols), run, compare)
+        leg["single_thread"] = moe_single_thread(bits, ends)
+        return leg
 
     config = {"workload": label % (rows, cols, g), "rows": rows, "cols": cols, "groups": g}
     return step, nb, timer, kb, name, cpu_baseline, config
@@ -766,7 +790,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="square16384", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cold-launches", type=int, default=20,
+    ap.add_argument("--cold-launches", type=int, default=50,
                     help="steps timed one by one after cache-evicting traffic (0: skip)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
