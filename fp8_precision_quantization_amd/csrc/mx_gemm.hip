@@ -118,6 +118,10 @@ __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
   // runs its piece of every group, one group after the other, the group
   // with the longest K range first (the groups' K lengths differ widely,
   // and short tiles last keep the CUs' finishing times close together).
+  // Grouped along M the same holds: each group's tiles are cut into 8
+  // pieces and the XCDs run the groups one after another, so that the
+  // chip works on one group's weights at a time (all groups' weights at
+  // once would not fit the memory-side cache next to A).
   const uint32_t tiles = a.tiles_m * a.tiles_n;
   uint32_t id = (blockIdx.x % 8) * a.per_xcd + blockIdx.x / 8;
   uint32_t kslot = 0;   // grouped along K: this tile's place in the group order
@@ -127,13 +131,19 @@ __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
     if (kslot >= (uint32_t)a.groups)
       return;  // uniform, before any barrier
   }
-  if (id >= tiles)
+  if (MODE != kGemmGroupsM && id >= tiles)
     return;  // uniform, before any barrier
-  const uint32_t band = id / (kGemmBand * a.tiles_n);
-  const uint32_t band_rows = min((uint32_t)kGemmBand, a.tiles_m - band * kGemmBand);
-  const uint32_t within = id - band * kGemmBand * a.tiles_n;
-  const uint32_t tm = band * kGemmBand + within % band_rows;
-  const uint32_t tn = within / band_rows;
+  // band order over a grid of tile rows: bands of 8 tile rows, column by column
+  auto band_tile = [&](uint32_t i, uint32_t rows_of_tiles, uint32_t& m_t, uint32_t& n_t) {
+    const uint32_t band = i / (kGemmBand * a.tiles_n);
+    const uint32_t band_rows = min((uint32_t)kGemmBand, rows_of_tiles - band * kGemmBand);
+    const uint32_t within = i - band * kGemmBand * a.tiles_n;
+    m_t = band * kGemmBand + within % band_rows;
+    n_t = within / band_rows;
+  };
+  uint32_t tm = 0, tn = 0;
+  if constexpr (MODE != kGemmGroupsM)
+    band_tile(id, a.tiles_m, tm, tn);
 
   // k: the reduction length of this tile; ld: the operands' row length
   int64_t k = a.k;
@@ -195,24 +205,46 @@ __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
     rows_valid = min((int64_t)kGemmTile, a.m - row0);
     srow0 = row0;
   } else if constexpr (GROUPED) {
-    // The group table borrows the B half of LDS stage 1 until the first
-    // stages are loaded.  (One LDS object keeps the compiler able to tell
-    // the loads into one stage from the reads of the other.)
-    static_assert(sizeof(GroupTable) <= kGemmStageBytes, "group table fits a stage half");
+    // The group table and the XCD piece starts borrow the B half of LDS
+    // stage 1 until the first stages are loaded.  (One LDS object keeps the
+    // compiler able to tell the loads into one stage from the reads of the
+    // other.)
+    static_assert(sizeof(GroupTable) + (MX_MAX_GROUPS + 1) * sizeof(int32_t) <= kGemmStageBytes,
+                  "group tables fit a stage half");
     GroupTable& table = *reinterpret_cast<GroupTable*>(lds[1][1]);
-    if (threadIdx.x < 64)
+    int32_t* xs = reinterpret_cast<int32_t*>(lds[1][1] + sizeof(GroupTable));
+    if (threadIdx.x < 64) {
       build_group_table(a.ends, a.groups, (int32_t)a.m, kGemmTile, table);
+      build_piece_starts(table, a.groups, kGemmTile, a.tiles_n, xs);
+    }
     lds_barrier();
     // Values read from LDS are per-lane to the compiler; readfirstlane
     // makes them scalar (they are the same in every lane), so that the
     // buffer descriptors built from them stay in scalar registers.
-    const int32_t pos = (int32_t)tm * kGemmTile;
-    const int g = __builtin_amdgcn_readfirstlane(find_group(table, a.groups, pos));
-    if (g < 0)
+    // XCD x's p-th tile: piece p - xs[g] of group g, the last g with
+    // xs[g] <= p (xs[G] = the pieces per XCD in all).
+    const int32_t p = (int32_t)(blockIdx.x / 8), x = (int32_t)(blockIdx.x % 8);
+    if (p >= __builtin_amdgcn_readfirstlane(xs[a.groups]))
       return;  // uniform; no barrier follows
+    int glo = 0, ghi = a.groups;   // xs[glo] <= p < xs[ghi]
+    while (ghi - glo > 1) {
+      const int mid = (glo + ghi) >> 1;
+      if (xs[mid] <= p)
+        glo = mid;
+      else
+        ghi = mid;
+    }
+    const int g = __builtin_amdgcn_readfirstlane(glo);
     const int32_t lo = __builtin_amdgcn_readfirstlane(table.lo[g]);
     const int32_t hi = __builtin_amdgcn_readfirstlane(table.hi[g]);
-    const int32_t r0 = lo + (pos - __builtin_amdgcn_readfirstlane(table.start[g]));
+    const uint32_t trows = (uint32_t)(__builtin_amdgcn_readfirstlane(table.start[g + 1]) -
+                                      __builtin_amdgcn_readfirstlane(table.start[g])) / kGemmTile;
+    const uint32_t tg = trows * a.tiles_n, pg = (tg + 7) / 8;
+    const uint32_t idx = (uint32_t)x * pg + (uint32_t)(p - __builtin_amdgcn_readfirstlane(xs[g]));
+    if (idx >= tg)
+      return;  // uniform; no barrier follows
+    band_tile(idx, trows, tm, tn);
+    const int32_t r0 = lo + (int32_t)tm * kGemmTile;
     row0 = r0;
     rows_valid = min(kGemmTile, hi - r0);
     // the tile's first row in A's M-grouped blocked scales: group g starts
@@ -221,7 +253,7 @@ __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
     for (int q = threadIdx.x & 63; q < g; q += 64)
       part += (table.hi[q] - table.lo[q] + 127) / 128 * 128;
     srow0 = __builtin_amdgcn_readfirstlane(wave_sum(part)) + (r0 - lo);
-    lds_barrier();   // every wave is done with the table
+    lds_barrier();   // every wave is done with the tables
     qb += (int64_t)g * a.n * ld;
     sb += (int64_t)g * a.sb_bytes;
   } else {
@@ -482,7 +514,9 @@ static GemmArgs gemm_args(const uint8_t* qa, const uint8_t* sa, const uint8_t* q
   const int64_t tn = (n + kGemmTile - 1) / kGemmTile;
   a.tiles_m = (uint32_t)tm;
   a.tiles_n = (uint32_t)tn;
-  const int64_t per = (tm * tn + 7) / 8;
+  // grouped along M each group's tiles are cut into 8 pieces of ceil(T_g /
+  // 8): in all at most ceil(tm * tn / 8) + groups per XCD
+  const int64_t per = (tm * tn + 7) / 8 + (mode == kGemmGroupsM ? groups : 0);
   a.per_xcd = (uint32_t)per;
   *blocks = per * 8 * (mode == kGemmGroupsK ? groups : 1);
   return a;

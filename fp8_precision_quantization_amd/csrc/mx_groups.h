@@ -105,6 +105,32 @@ __device__ __forceinline__ int find_source_group(const GroupTable& t, int groups
   return lo;
 }
 
+// Starts of each group's piece of an XCD's work in the grouped GEMM: group g
+// has T_g = (start[g + 1] - start[g]) / unit * tiles_n tiles, cut into 8
+// pieces of P_g = ceil(T_g / 8) (one per XCD); xs[g] = sum of the earlier
+// P_h, xs[G] the total.  Wave 0 fills it after the row table.
+__device__ inline void build_piece_starts(const GroupTable& t, int groups, int32_t unit, uint32_t tiles_n,
+                                          int32_t* xs) {
+  const int lane = threadIdx.x & 63;
+  const int per = (groups + 63) / 64;
+  const int g0 = min(lane * per, groups), g1 = min(g0 + per, groups);
+  auto pieces = [&](int g) {
+    return (int32_t)(((uint32_t)((t.start[g + 1] - t.start[g]) / unit) * tiles_n + 7) / 8);
+  };
+  int32_t local = 0;
+  for (int g = g0; g < g1; ++g)
+    local += pieces(g);
+  const int32_t incl = wave_incl_sum(local, lane);
+  int32_t run = incl - local;
+  for (int g = g0; g < g1; ++g) {
+    xs[g] = run;
+    run += pieces(g);
+  }
+  const int32_t total = __shfl(incl, 63);
+  if (lane == 0)
+    xs[groups] = total;
+}
+
 // Starts of the K-grouped blocked scales of row groups: group g covers scale
 // columns (32-row blocks) [lo_g / 32, hi_g / 32) of its clamped row range,
 // padded to a multiple of 4; kstart[g] = sum of the earlier padded widths,

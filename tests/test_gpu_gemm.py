@@ -93,7 +93,9 @@ def test_gemm_zero_k_and_empty():
 
 
 GROUP_CASES = [("one", 500, [500]), ("four", 1000, [100, 100, 613, 1000]), ("ragged", 777, [1, 130, 700, 777]),
-               ("malformed", 600, [300, 200, 900, 600]), ("short", 600, [128, 300])]
+               ("malformed", 600, [300, 200, 900, 600]), ("short", 600, [128, 300]),
+               ("many", 2000, [29 * i for i in range(1, 70)] + [2000]),   # 70 groups, some spanning 2 tiles
+               ("tall", 1800, [40, 1700, 1800])]                            # a group of 7 tile rows (one band)
 
 
 @pytest.mark.parametrize("name,m,ends", GROUP_CASES, ids=[c[0] for c in GROUP_CASES])

@@ -103,3 +103,27 @@ def test_random_kgrouped_gemm(oracle_mod, seed):
     for gi, (want, absum) in enumerate(gemm_t._kgroup_ref(oracle_mod, qa, sa, qb, sb, ends, k)):
         gemm_t._check(out[gi], want, absum, False, "seed %d (%d, %d, %d) ends %s group %d"
                       % (seed, m, n, k, ends, gi))
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_mgrouped_gemm(oracle_mod, seed):
+    dev = device()
+    rng = np.random.default_rng([410, seed])
+    m, n = int(rng.integers(1, 1500)), int(rng.integers(1, 300))
+    k = 32 * int(rng.integers(1, 20))
+    ends = _ends(rng, m, int(rng.integers(1, 300)))
+    g = len(ends)
+    qa, sa = gemm_t._codes_scales(m, k, [411, seed])
+    qb = np.stack([gemm_t._codes_scales(n, k, [412, seed, i])[0] for i in range(g)])
+    sb = np.stack([gemm_t._codes_scales(n, k, [412, seed, i])[1] for i in range(g)])
+    e = np.asarray(ends, np.int32)
+    want, absum = oracle_mod.mx_gemm_grouped(qa, sa, qb, sb, e)
+    out = torch.full((m, n), 12345.0, device=dev)
+    mx.mx_grouped_gemm_mxfp8(to_dev_u8(qa, dev), gemm_t._blocked_m_groups(oracle_mod, sa, ends, dev),
+                             to_dev_u8(qb, dev), gemm_t._blocked(oracle_mod, sb, dev), torch.from_numpy(e).to(dev),
+                             out_dtype=torch.float32, out=out)
+    torch.cuda.synchronize(dev)
+    rows = ~np.isnan(want[:, 0])
+    what = "seed %d (%d, %d, %d) ends %s" % (seed, m, n, k, ends)
+    gemm_t._check(out[torch.from_numpy(rows).to(dev)], want[rows], absum[rows], False, what)
+    assert torch.all(out[torch.from_numpy(~rows).to(dev)] == 12345.0), what + ": rows past the last end written"
