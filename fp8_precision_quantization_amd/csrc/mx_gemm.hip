@@ -469,7 +469,55 @@ __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
     __builtin_amdgcn_s_waitcnt(0x0F70);
   }
 
-  // epilogue: register v of lane l is row 8 (v / 4) + 4 h + v % 4, column r
+  // Epilogue.  Register v of lane l holds row 8 (v / 4) + 4 h + v % 4,
+  // column r of its 32 x 32 block.  bf16 output with rows of whole 16-byte
+  // chunks (n % 8 == 0, c 16-byte aligned): the tile goes through LDS (the
+  // operand stages are free now; 256 x 256 bf16 is exactly their 128 KiB)
+  // and leaves as 512-byte rows of 16-byte stores -- written straight from
+  // the registers it would take 2-byte stores, 1024 instructions per
+  // workgroup, and measured a fifth of the GEMM's time.  In LDS, dword d of
+  // row R (columns 2 d, 2 d + 1) sits at d ^ swz(R), swz(R) = 16 (2 ((R >> 2)
+  // & 1) + (R & 1)): the four rows one write instruction touches (R, R + 1,
+  // R + 4, R + 5) land on different 16-bank groups, and a 16-byte chunk
+  // stays whole.
+  if constexpr (BF16) {
+    if ((a.n & 7) == 0 && (reinterpret_cast<uintptr_t>(c) & 15) == 0) {
+      uint32_t* ldsw = reinterpret_cast<uint32_t*>(&lds[0][0][0]);
+      auto swz = [](int row) { return 16 * (2 * ((row >> 2) & 1) + (row & 1)); };
+      lds_barrier();   // every wave is done reading operands from LDS
+      const bool odd = (r & 1) != 0;
+#pragma unroll
+      for (int i = 0; i < kGemmWaveBlocks; ++i)
+#pragma unroll
+        for (int j = 0; j < kGemmWaveBlocks; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; v += 2) {
+            // rows R and R + 1 of column r; lanes r and r ^ 1 trade so that
+            // the even lane writes row R and the odd lane row R + 1, each as
+            // the bf16 pair of columns r & ~1 and (r & ~1) + 1
+            const uint32_t lo16 = to_bf16(acc[i][j][v]), hi16 = to_bf16(acc[i][j][v + 1]);
+            const uint32_t recv = quad_swap1(odd ? lo16 : hi16);
+            const uint32_t word = odd ? (recv | (hi16 << 16)) : (lo16 | (recv << 16));
+            const int row = wm * 128 + 32 * i + 8 * (v / 4) + 4 * h + (v % 4) + (odd ? 1 : 0);
+            const int d = wn * 64 + 16 * j + (r >> 1);
+            ldsw[row * 128 + (d ^ swz(row))] = word;
+          }
+      lds_barrier();
+      // thread t: 16-byte chunk t % 32 of rows t / 32 + 8 p
+      const int chunk = threadIdx.x & 31;
+      const bool col_on = 8 * chunk < cols_valid;
+      uint8_t* cb = static_cast<uint8_t*>(c) + ((row0 * a.n + col0) * 2 + 16 * chunk);
+#pragma unroll 8
+      for (int p = 0; p < kGemmTile / 8; ++p) {
+        const int row = (threadIdx.x >> 5) + 8 * p;
+        if (row < rows_valid && col_on) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(&ldsw[row * 128 + ((4 * chunk) ^ swz(row))]);
+          __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(cb + (int64_t)row * a.n * 2));
+        }
+      }
+      return;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < kGemmWaveBlocks; ++i)
 #pragma unroll
