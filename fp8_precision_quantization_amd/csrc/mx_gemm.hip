@@ -517,6 +517,45 @@ __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
       }
       return;
     }
+  } else {
+    // fp32 output, rows of whole 16-byte chunks (n % 4 == 0): the same in two
+    // passes of 128 rows (the waves with wm = pass write their quadrants),
+    // dword d of row R at d ^ (32 ((R >> 2) & 1)) so that rows R and R + 4
+    // of one write instruction use different banks.
+    if ((a.n & 3) == 0 && (reinterpret_cast<uintptr_t>(c) & 15) == 0) {
+      uint32_t* ldsw = reinterpret_cast<uint32_t*>(&lds[0][0][0]);
+      auto swz = [](int row) { return 32 * ((row >> 2) & 1); };
+      const int chunk = threadIdx.x & 63;
+      const bool col_on = 4 * chunk < cols_valid;
+#pragma unroll
+      for (int pass = 0; pass < 2; ++pass) {
+        lds_barrier();   // operands (pass 0) or the previous pass (pass 1) are read
+        if (wm == pass) {
+#pragma unroll
+          for (int i = 0; i < kGemmWaveBlocks; ++i)
+#pragma unroll
+            for (int j = 0; j < kGemmWaveBlocks; ++j)
+#pragma unroll
+              for (int v = 0; v < 16; ++v) {
+                const int row = 32 * i + 8 * (v / 4) + 4 * h + (v % 4);   // within the pass
+                const int d = wn * 128 + 32 * j + r;
+                ldsw[row * 256 + (d ^ swz(row))] = __float_as_uint(acc[i][j][v]);
+              }
+        }
+        lds_barrier();
+        // thread t: 16-byte chunk t % 64 of rows t / 64 + 4 p of the pass
+        uint8_t* cb = static_cast<uint8_t*>(c) + (((row0 + 128 * pass) * a.n + col0) * 4 + 16 * chunk);
+#pragma unroll 8
+        for (int p = 0; p < 32; ++p) {
+          const int row = (threadIdx.x >> 6) + 4 * p;
+          if (128 * pass + row < rows_valid && col_on) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(&ldsw[row * 256 + ((4 * chunk) ^ swz(row))]);
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(cb + (int64_t)row * a.n * 4));
+          }
+        }
+      }
+      return;
+    }
   }
 #pragma unroll
   for (int i = 0; i < kGemmWaveBlocks; ++i)
