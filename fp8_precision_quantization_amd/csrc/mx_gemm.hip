@@ -307,7 +307,7 @@ __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
   // K also the tile before it (combined when the scales are used, so that
   // no wait for the scale loads stands before the MFMAs that follow them)
   constexpr int kSW = MODE == kGemmGroupsK ? 2 * kGemmWaveBlocks : kGemmWaveBlocks;
-  uint32_t s0a[kSW], s0b[kSW], s1a[kSW], s1b[kSW];
+  uint32_t s0a[kSW], s0b[kSW], s1a[kSW] = {}, s1b[kSW] = {};
 
   // Load u (0 .. 15) of a stage: load instruction u / 2 of operand u % 2,
   // from memory straight into LDS half st.  Chunks outside [kofs, kofs + K)
@@ -326,26 +326,26 @@ __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
   // 32 i + r.  Blocks past K are the layout's zero padding (their data is
   // zero too); a stage past K reads zero.  With kofs = 32 d the stage's
   // blocks are the group's blocks 4 j - d .. 4 j - d + 3: the last d bytes
-  // of tile j - 1 and the first 4 - d of tile j (blocks before the group's
-  // first, tile -1, read zero, as their data does).
-  auto load_scales = [&](int kt, uint32_t (&s_a)[kSW], uint32_t (&s_b)[kSW]) {
+  // of tile j - 1 and the first 4 - d of tile j.  Tile j - 1 is the previous
+  // stage's tile, still in registers (prev; zero before the first stage,
+  // as the data of blocks before the group's first is): a copy, so that the
+  // stage issues no more loads than a dense one (the loads into LDS, not
+  // the MFMAs, bound these kernels).
+  auto load_scales = [&](int kt, uint32_t (&s_a)[kSW], uint32_t (&s_b)[kSW], const uint32_t (&prev_a)[kSW],
+                         const uint32_t (&prev_b)[kSW]) {
+    if constexpr (MODE == kGemmGroupsK) {
+#pragma unroll
+      for (int i = 0; i < kGemmWaveBlocks; ++i) {
+        s_a[kGemmWaveBlocks + i] = prev_a[i];
+        s_b[kGemmWaveBlocks + i] = prev_b[i];
+      }
+    }
     const u32x4 va = __builtin_amdgcn_raw_buffer_load_b128(rsa, 16 * r, kt / kGemmTK * 512, 0);
     const u32x4 vb = __builtin_amdgcn_raw_buffer_load_b128(rsb, 16 * r, kt / kGemmTK * 512, 0);
 #pragma unroll
     for (int i = 0; i < kGemmWaveBlocks; ++i) {
       s_a[i] = va[i];
       s_b[i] = vb[i];
-    }
-    if constexpr (MODE == kGemmGroupsK) {
-      // (with d = 0 none of its bytes is used: it loads zero, from no memory)
-      const int poff = kt >= kGemmTK && kofs != 0 ? 16 * r + (kt / kGemmTK - 1) * 512 : (int)0x80000000;
-      const u32x4 pa = __builtin_amdgcn_raw_buffer_load_b128(rsa, poff, 0, 0);
-      const u32x4 pb = __builtin_amdgcn_raw_buffer_load_b128(rsb, poff, 0, 0);
-#pragma unroll
-      for (int i = 0; i < kGemmWaveBlocks; ++i) {
-        s_a[kGemmWaveBlocks + i] = pa[i];
-        s_b[kGemmWaveBlocks + i] = pb[i];
-      }
     }
   };
   // MFMA operands of one step as 16-byte halves: [slab][0] = chunk 4 s + h
@@ -401,7 +401,7 @@ __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
                         const uint32_t (&cur_a)[kSW], const uint32_t (&cur_b)[kSW],
                         uint32_t (&nxt_a)[kSW], uint32_t (&nxt_b)[kSW], Half& f1a,
                         Half& f1b) {
-    load_scales(kt + kGemmTK, nxt_a, nxt_b);
+    load_scales(kt + kGemmTK, nxt_a, nxt_b, cur_a, cur_b);
     int xa[kGemmWaveBlocks], xb[kGemmWaveBlocks];
     step_scales(0, cur_a, xa);
     step_scales(0, cur_b, xb);
@@ -421,9 +421,9 @@ __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
     step_scales(1, cur_a, xa);
     step_scales(1, cur_b, xb);
     __builtin_amdgcn_sched_barrier(0);
-    // all but the scale loads of stage t + 1 (two, or four grouped along
-    // K): this wave's loads of stage t + 1 (vmcnt), then every wave's
-    __builtin_amdgcn_s_waitcnt(0x0F70 | (MODE == kGemmGroupsK ? 4 : 2));
+    // all but the two scale loads of stage t + 1: this wave's loads of
+    // stage t + 1 (vmcnt), then every wave's
+    __builtin_amdgcn_s_waitcnt(0x0F70 | 2);
     lds_barrier();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -450,7 +450,8 @@ __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
       load_one(S0(), 0, u);
       load_one(S1(), kGemmTK, u);
     }
-    load_scales(0, s0a, s0b);
+    // (s1 is zero here: the tile before the first stage's)
+    load_scales(0, s0a, s0b, s1a, s1b);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     lds_barrier();
     Half f0a, f0b, f1a, f1b;
