@@ -243,11 +243,22 @@ struct Stage {
 struct NoStage {};  // dim0-only casts stage nothing
 
 // Work order: groups of row_group row tiles; inside a group, column tiles
-// outermost; each XCD takes a contiguous run of this order.
+// outermost; each XCD takes a contiguous run of this order, starting at a
+// point of its own within the run.
 __device__ __forceinline__ bool tile_of(uint32_t bid, uint32_t row_tiles, uint32_t col_tiles,
-                                        uint32_t per_xcd, uint32_t row_group, uint32_t& rt,
+                                        uint32_t per_xcd, uint32_t row_group, bool rotate, uint32_t& rt,
                                         uint32_t& ct) {
-  const uint32_t id = (bid % kXcds) * per_xcd + bid / kXcds;
+  // rotate (casts whose stores all write whole lines): XCD x starts its
+  // piece x quarters of a piece in, wrapping round.  With every XCD at the
+  // start of its piece, XCDs whose pieces begin a large power of two of rows
+  // apart write the col-major output at addresses a large power of two apart
+  // at the same moment, which cost up to a fifth of the time (blocked
+  // scales, 32768 x 8192: 199 -> 162 us rotated; 16384 x 16384 and
+  // 16640 x 5120 unchanged).  The casts with plain or grouped scales keep
+  // the plain order: their partial scale lines merge in the L2 of the XCD
+  // that runs the neighbouring tiles, and rotated they ran 2-4% slower.
+  const uint32_t x = bid % kXcds, p = bid / kXcds;
+  const uint32_t id = x * per_xcd + (rotate ? (p + x * (per_xcd / 4)) % per_xcd : p);
   if (id >= row_tiles * col_tiles)
     return false;
   const uint32_t group_items = row_group * col_tiles;
@@ -461,7 +472,7 @@ __global__ __launch_bounds__(256) void cast_kernel(CastArgs a) {
   __shared__ std::conditional_t<KGRP, KStarts, NoKStarts> kstarts;
 
   uint32_t rt, ct;
-  if (!tile_of(blockIdx.x, a.row_tiles, a.col_tiles, a.per_xcd, a.row_group, rt, ct))
+  if (!tile_of(blockIdx.x, a.row_tiles, a.col_tiles, a.per_xcd, a.row_group, BLK || !DIM0, rt, ct))
     return;  // uniform over the workgroup
   // The wave index is uniform; saying so keeps the buffer descriptors built
   // from it in scalar registers.
