@@ -46,7 +46,11 @@ def mixed_rows(rows, cols, seed):
 # 1/2/4/8 chunks per lane, workgroup per row with 4/8/16), the boundaries
 # between them, ragged row tails, and the two-pass kernel past 32768 columns
 SHAPES = [(1024, 2048), (4096, 2048), (7, 8), (5, 64), (33, 512), (17, 520), (9, 1024), (10, 2048),
-          (6, 4096), (5, 4104), (3, 8192), (4, 8200), (2, 16384), (3, 32768), (2, 32776), (2, 40000)]
+          (6, 4096), (5, 4104), (3, 8192), (4, 8200), (2, 16384), (3, 32768), (2, 32776), (2, 40000),
+          # widths between the powers of two, where some chunk slots of a lane stay empty
+          # (common model widths among them)
+          (7, 3072), (9, 5120), (1024, 5120), (5, 6144), (3, 7168), (5, 12288), (3, 14336), (3, 18432),
+          (2, 24576), (3, 28672), (5, 5128)]
 
 
 @pytest.mark.parametrize("shape", SHAPES)
