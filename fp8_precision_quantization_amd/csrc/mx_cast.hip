@@ -219,6 +219,7 @@ struct CastArgs {
   int64_t rows, cols, rows_per_seg;
   uint32_t row_tiles, col_tiles, per_xcd;
   uint32_t row_group;  // row bands that run side by side on one XCD
+  uint32_t rotate;     // XCD pieces start at points of their own (tile_of)
   // Blocked scale outputs: column blocks of the dim0 scale matrix, of one
   // segment's dim1 scale matrix, and that matrix's size in bytes.
   int64_t ncb0, ncb1, seg_blk_bytes;
@@ -248,15 +249,8 @@ struct NoStage {};  // dim0-only casts stage nothing
 __device__ __forceinline__ bool tile_of(uint32_t bid, uint32_t row_tiles, uint32_t col_tiles,
                                         uint32_t per_xcd, uint32_t row_group, bool rotate, uint32_t& rt,
                                         uint32_t& ct) {
-  // rotate (casts whose stores all write whole lines): XCD x starts its
-  // piece x quarters of a piece in, wrapping round.  With every XCD at the
-  // start of its piece, XCDs whose pieces begin a large power of two of rows
-  // apart write the col-major output at addresses a large power of two apart
-  // at the same moment, which cost up to a fifth of the time (blocked
-  // scales, 32768 x 8192: 199 -> 162 us rotated; 16384 x 16384 and
-  // 16640 x 5120 unchanged).  The casts with plain or grouped scales keep
-  // the plain order: their partial scale lines merge in the L2 of the XCD
-  // that runs the neighbouring tiles, and rotated they ran 2-4% slower.
+  // rotate: XCD x starts its piece x quarters of a piece in, wrapping round
+  // (when it pays; see cast_args).
   const uint32_t x = bid % kXcds, p = bid / kXcds;
   const uint32_t id = x * per_xcd + (rotate ? (p + x * (per_xcd / 4)) % per_xcd : p);
   if (id >= row_tiles * col_tiles)
@@ -472,7 +466,7 @@ __global__ __launch_bounds__(256) void cast_kernel(CastArgs a) {
   __shared__ std::conditional_t<KGRP, KStarts, NoKStarts> kstarts;
 
   uint32_t rt, ct;
-  if (!tile_of(blockIdx.x, a.row_tiles, a.col_tiles, a.per_xcd, a.row_group, BLK || !DIM0, rt, ct))
+  if (!tile_of(blockIdx.x, a.row_tiles, a.col_tiles, a.per_xcd, a.row_group, a.rotate != 0, rt, ct))
     return;  // uniform over the workgroup
   // The wave index is uniform; saying so keeps the buffer descriptors built
   // from it in scalar registers.
@@ -695,6 +689,17 @@ static CastArgs cast_args(const uint16_t* x, int64_t rows, int64_t cols, int64_t
   // one after another; 353 us at (16 * 8192) x 5120 against 361 with 512
   // and 371 with 256 row tiles).
   a.row_group = q0 != nullptr ? (blocked ? kRowGroupBlocked : kRowGroupPlain) : kRowGroupDim1;
+  // With every XCD at the start of its piece, XCDs whose pieces begin a
+  // multiple of 4 KiB apart in the col-major output (pieces of whole row
+  // bands, per / ct row tiles of 128 bytes there, a multiple of 32) write it
+  // at addresses that far apart at the same moment, which cost up to a fifth
+  // of the time; starting each XCD at a point of its own removes that
+  // (32768 x 8192, blocked scales: 199 -> 163 us; 65536 x 5120, plain or
+  // grouped scales: 292-297 -> 263 us).  Where the pieces start elsewhere
+  // the plain start is as fast or faster (16384 x 16384 with plain or
+  // grouped scales: 185 against 193 us rotated).  The dim1-only casts run
+  // whole column strips per XCD: rotated, 0.5-1% faster.
+  a.rotate = q0 == nullptr || (per % ct == 0 && (per / ct) % 32 == 0) ? 1u : 0u;
   a.ends = nullptr;
   a.groups = 0;
   a.out_starts = nullptr;
