@@ -82,9 +82,14 @@ __global__ __launch_bounds__(kBlkThreads) void blocked_kernel(Args a) {
   const int64_t b = bid / a.row_blocks;
 
   if constexpr (MODE != kModeBatched) {
-    if (tid < 64)
-      build_group_table(a.ends, a.groups, (int32_t)(MODE == kModeMGroups ? a.rows : a.cols),
-                        MODE == kModeMGroups ? kTileRows : 4, table);
+    if (tid < 64) {
+      const int32_t extent = (int32_t)(MODE == kModeMGroups ? a.rows : a.cols);
+      const int32_t unit = MODE == kModeMGroups ? kTileRows : 4;
+      if (a.groups <= kScalarTableGroups)
+        build_group_table_scalar(a.ends, a.groups, extent, unit, table);
+      else
+        build_group_table(a.ends, a.groups, extent, unit, table);
+    }
     __syncthreads();
     if (bid == 0 && a.out_starts != nullptr) {
       for (int g = tid; g <= a.groups; g += kBlkThreads)

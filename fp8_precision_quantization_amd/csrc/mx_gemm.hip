@@ -171,7 +171,10 @@ __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
     KStarts& kst = *reinterpret_cast<KStarts*>(lds[1][1] + sizeof(GroupTable));
     int32_t* order = reinterpret_cast<int32_t*>(lds[1][1] + sizeof(GroupTable) + sizeof(KStarts));
     if (threadIdx.x < 64) {
-      build_group_table(a.ends, a.groups, (int32_t)a.k, 32, table);
+      if (a.groups <= kScalarTableGroups)
+        build_group_table_scalar(a.ends, a.groups, (int32_t)a.k, 32, table);
+      else
+        build_group_table(a.ends, a.groups, (int32_t)a.k, 32, table);
       build_kstarts(table, a.groups, kst);
       // up to 64 groups: longest block count first, ties by index (lane g
       // counts the groups that go before it)
@@ -214,7 +217,10 @@ __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
     GroupTable& table = *reinterpret_cast<GroupTable*>(lds[1][1]);
     int32_t* xs = reinterpret_cast<int32_t*>(lds[1][1] + sizeof(GroupTable));
     if (threadIdx.x < 64) {
-      build_group_table(a.ends, a.groups, (int32_t)a.m, kGemmTile, table);
+      if (a.groups <= kScalarTableGroups)
+        build_group_table_scalar(a.ends, a.groups, (int32_t)a.m, kGemmTile, table);
+      else
+        build_group_table(a.ends, a.groups, (int32_t)a.m, kGemmTile, table);
       build_piece_starts(table, a.groups, kGemmTile, a.tiles_n, xs);
     }
     lds_barrier();

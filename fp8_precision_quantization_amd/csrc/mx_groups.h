@@ -74,6 +74,31 @@ __device__ inline void build_group_table(const int32_t* __restrict__ ends, int g
     t.start[groups] = total;
 }
 
+// The same table for a few groups, by one wave in a uniform loop: the ends
+// are read with scalar loads, which every workgroup after the first on a CU
+// finds in the scalar cache (the vector loads of build_group_table go to the
+// L2 each time, a round trip the grouped layouts wait for before their
+// first data load).  Lane 0 writes the table.
+constexpr int kScalarTableGroups = 32;
+__device__ inline void build_group_table_scalar(const int32_t* __restrict__ ends, int groups, int32_t extent,
+                                                int32_t unit, GroupTable& t) {
+  const bool writer = (threadIdx.x & 63) == 0;
+  int32_t run = 0, prev = 0, start = 0;
+  for (int g = 0; g < groups; ++g) {
+    run = max(run, ends[g]);
+    const int32_t e = min(run, extent);
+    if (writer) {
+      t.lo[g] = prev;
+      t.hi[g] = e;
+      t.start[g] = start;
+    }
+    start += (e - prev + unit - 1) / unit * unit;
+    prev = e;
+  }
+  if (writer)
+    t.start[groups] = start;
+}
+
 // Last g in [0, groups) with start[g] <= pos, or -1 if pos >= start[groups].
 __device__ __forceinline__ int find_group(const GroupTable& t, int groups, int32_t pos) {
   if (pos >= t.start[groups])
