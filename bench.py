@@ -684,29 +684,68 @@ def setup_tensorwise(dev, n=16384):
     return step, nb, timer, nb, "tensor-wise fp8 cast (amax + cast launches)", cpu_baseline, config
 
 
-def _mx_operands(rows, k, seed, dev):
+def _mx_host(rows, k, seed):
     """Seeded random finite e4m3 codes and e8m0 scales (2^-9 .. 2^8)."""
     rng = np.random.default_rng(seed)
     q = rng.integers(0, 256, size=(rows, k), dtype=np.uint8)
     q[(q & 0x7F) == 0x7F] = 0x7E
     s = rng.integers(118, 136, size=(rows, k // 32), dtype=np.uint8)
+    return q, s
+
+
+def _mx_operands(rows, k, seed, dev):
+    q, s = _mx_host(rows, k, seed)
     return torch.from_numpy(q).to(dev), torch.from_numpy(s).to(dev)
+
+
+GEMM_SAMPLE_ROWS = 32
+
+
+def gemm_oracle_leg(c_rows, parts, n, k, what):
+    """The oracle's fp64 GEMM on a bounded sample: the first
+    GEMM_SAMPLE_ROWS rows of A against all of B, summed over `parts`
+    ((qa, sa, qb, sb) host operands whose products add up to those rows of
+    C), timed on the host; the GPU's rows `c_rows` (bf16) must lie within
+    2^-10 of the sum of |products| plus half a bf16 ulp."""
+    import oracle
+    t0 = time.perf_counter()
+    want = 0.0
+    absum = 0.0
+    for qa, sa, qb, sb in parts:
+        c, ab = oracle.mx_gemm(qa, sa, qb, sb)
+        want = want + c
+        absum = absum + ab
+    dt = time.perf_counter() - t0
+    got = c_rows.float().cpu().numpy().astype(np.float64)
+    tol = 2.0 ** -10 * absum + np.abs(want) * 2.0 ** -8 + 1e-30
+    bad = int(np.count_nonzero(np.abs(got - want) > tol))
+    flops = 2 * GEMM_SAMPLE_ROWS * n * k
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "%s: the first %d rows of C (%d x %d x %d), fp64, %.1f s wall"
+                      % (what, GEMM_SAMPLE_ROWS, GEMM_SAMPLE_ROWS, n, k, dt),
+            "matches_gpu": bad == 0, **({} if bad == 0 else {"outside_tolerance": bad})}
 
 
 def setup_gemm(dev, grouped=False, m=16640, n=8192, k=5120):
     log("generating MX operands")
-    qa, sa = _mx_operands(m, k, 101, dev)
+    qa_h, sa_h = _mx_host(m, k, 101)
+    qa, sa = torch.from_numpy(qa_h).to(dev), torch.from_numpy(sa_h).to(dev)
     # scales in the blocked layouts the GEMM reads (arranged before timing)
     if grouped:
         _, ends = workloads.moe_activations()
         g = len(ends)
-        ops = [_mx_operands(n, k, 200 + i, dev) for i in range(g)]
-        qb = torch.stack([o[0] for o in ops])
-        sb = mx.mx_scales_to_blocked(torch.stack([o[1] for o in ops]), raw=True)
+        hb = [_mx_host(n, k, 200 + i) for i in range(g)]
+        qb = torch.from_numpy(np.stack([o[0] for o in hb])).to(dev)
+        sb = mx.mx_scales_to_blocked(torch.from_numpy(np.stack([o[1] for o in hb])).to(dev), raw=True)
         offs = torch.from_numpy(ends).to(dev)
         sa = mx.mx_scales_to_blocked_grouped(sa, offs, 0, raw=True)[0]
+        # the sampled rows lie in group 0 (1440 rows)
+        assert ends[0] >= GEMM_SAMPLE_ROWS
+        sample_b = hb[0]
     else:
-        qb, sb = _mx_operands(n, k, 102, dev)
+        sample_b = _mx_host(n, k, 102)
+        qb, sb = torch.from_numpy(sample_b[0]).to(dev), torch.from_numpy(sample_b[1]).to(dev)
         sa = mx.mx_scales_to_blocked(sa, raw=True)
         sb = mx.mx_scales_to_blocked(sb, raw=True)
     c = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
@@ -723,6 +762,12 @@ def setup_gemm(dev, grouped=False, m=16640, n=8192, k=5120):
             call()
 
     flops = 2 * m * n * k
+
+    def cpu_baseline():
+        r = GEMM_SAMPLE_ROWS
+        return gemm_oracle_leg(c[:r], [(qa_h[:r], sa_h[:r], sample_b[0], sample_b[1])], n, k,
+                               "grouped along M, group 0" if grouped else "dense")
+
     config = {"workload": "%s M=%d N=%d K=%d, e4m3 x e4m3 with e8m0 block scales (blocked layout), bf16 out%s"
                           % ("mx_grouped_gemm_mxfp8" if grouped else "mx_gemm_mxfp8", m, n, k,
                              ", 4 groups along M" if grouped else ""),
@@ -731,7 +776,7 @@ def setup_gemm(dev, grouped=False, m=16640, n=8192, k=5120):
                         % ("grouped " if grouped else ""),
               "dtype": "e4m3",
               "flops": flops}
-    return step, flops, timer, flops, "MX GEMM" + (" grouped" if grouped else ""), None, config
+    return step, flops, timer, flops, "MX GEMM" + (" grouped" if grouped else ""), cpu_baseline, config
 
 
 def setup_ggemm(dev):
@@ -746,8 +791,10 @@ def setup_kggemm(dev, m=8192, n=5120, k=16640):
     g = len(ends)
     offs = torch.from_numpy(ends).to(dev)
     kends = torch.from_numpy(ends // 32).to(dev)
-    qa, sa = _mx_operands(m, k, 111, dev)
-    qb, sb = _mx_operands(n, k, 112, dev)
+    qa_h, sa_h = _mx_host(m, k, 111)
+    qb_h, sb_h = _mx_host(n, k, 112)
+    qa, sa = torch.from_numpy(qa_h).to(dev), torch.from_numpy(sa_h).to(dev)
+    qb, sb = torch.from_numpy(qb_h).to(dev), torch.from_numpy(sb_h).to(dev)
     sa = mx.mx_scales_to_blocked_grouped(sa, kends, 1, raw=True)[0]
     sb = mx.mx_scales_to_blocked_grouped(sb, kends, 1, raw=True)[0]
     c = torch.empty((g, m, n), dtype=torch.bfloat16, device=dev)
@@ -760,13 +807,34 @@ def setup_kggemm(dev, m=8192, n=5120, k=16640):
             call()
 
     flops = 2 * m * n * k
+
+    def cpu_baseline():
+        # the first rows of every group's output: per group, its K range
+        r = GEMM_SAMPLE_ROWS
+        legs = []
+        lo = 0
+        for gi, e in enumerate(ends):
+            hi = min(max(int(e), lo), k)
+            kl, kh = lo // 32, hi // 32
+            legs.append(gemm_oracle_leg(c[gi, :r], [(qa_h[:r, 32 * kl:32 * kh], sa_h[:r, kl:kh],
+                                                    qb_h[:, 32 * kl:32 * kh], sb_h[:, kl:kh])], n, 32 * (kh - kl),
+                                        "group %d" % gi))
+            lo = hi
+        secs = sum(float(re.search(r"([0-9.]+) s wall", leg["sample"]).group(1)) for leg in legs)
+        ok = all(leg["matches_gpu"] for leg in legs)
+        return {"value": round(2 * r * n * k / max(secs, 1e-9) / 1e12, 6), "unit": "TFLOP/s",
+                "cores": legs[0]["cores"], "kind": "oracle",
+                "sample": "the first %d rows of each of the %d outputs (%d x %d, each over its group's K range), "
+                          "fp64, %.1f s wall" % (r, len(legs), r, n, secs),
+                "matches_gpu": ok}
+
     config = {"workload": "mx_kgrouped_gemm_mxfp8 M=%d N=%d K=%d tokens in %d groups along K, e4m3 x e4m3 with "
                           "e8m0 block scales (K-grouped blocked layout), bf16 out" % (m, n, k, g),
               "m": m, "n": n, "k": k, "groups": g, "unit": "TFLOP/s", "bound": "mfma",
               "peak": MFMA_FP8_PEAK_TFLOPS,
               "metric": "achieved TFLOP/s of the MX-scaled GEMM grouped along K (% of MI355X dense fp8 MFMA peak)",
               "dtype": "e4m3", "flops": flops}
-    return step, flops, timer, flops, "MX GEMM grouped along K", None, config
+    return step, flops, timer, flops, "MX GEMM grouped along K", cpu_baseline, config
 
 
 def _device_normal_bf16(rows, cols, seed, dev):
