@@ -41,14 +41,21 @@
 // zero padding.  Tiles are ordered in bands of 8 tile rows, column by
 // column, and the ordered list is cut into 8 contiguous pieces, one per XCD
 // (workgroups are dealt to the XCDs round-robin), so that each XCD's L2
-// sees a compact region of A rows and B columns.
+// sees a compact region of A rows and B columns.  The output tile leaves
+// through LDS as whole rows of 16-byte stores (the epilogue below).
 //
-// Grouped along M (GROUPED): the tiles of group g cover its rows [lo_g,
-// hi_g) in 256-row steps from the group's padded start (the group table of
-// the blocked layouts, rebuilt from the device offsets in each workgroup);
-// A's scales are the M-grouped blocked layout (groups padded to 128 rows),
-// B and its scales are group g's (N, K) slice.  Rows past the last end are
-// not written.
+// Grouped along M: the tiles of group g cover its rows [lo_g, hi_g) in
+// 256-row steps (the group table of the blocked layouts, rebuilt from the
+// device offsets in each workgroup); A's scales are the M-grouped blocked
+// layout (groups padded to 128 rows), B and its scales are group g's (N, K)
+// slice.  Rows past the last end are not written.
+//
+// Grouped along K (the weight gradient): one (M, N) output per group, over
+// the group's K range; the scales are the K-grouped blocked layouts.
+//
+// Grouped either way, each group's ordered tiles are cut into 8 pieces, one
+// per XCD, and an XCD runs its pieces group after group, so that the chip
+// streams one group's operands at a time.
 #include "mx_device.h"
 #include "mx_groups.h"
 #include "mxcast.h"
