@@ -695,11 +695,13 @@ static CastArgs cast_args(const uint16_t* x, int64_t rows, int64_t cols, int64_t
   // at addresses that far apart at the same moment, which cost up to a fifth
   // of the time; starting each XCD at a point of its own removes that
   // (32768 x 8192, blocked scales: 199 -> 163 us; 65536 x 5120, plain or
-  // grouped scales: 292-297 -> 263 us).  Where the pieces start elsewhere
-  // the plain start is as fast or faster (16384 x 16384 with plain or
-  // grouped scales: 185 against 193 us rotated).  The dim1-only casts run
-  // whole column strips per XCD: rotated, 0.5-1% faster.
-  a.rotate = q0 == nullptr || (per % ct == 0 && (per / ct) % 32 == 0) ? 1u : 0u;
+  // grouped scales: 292-297 -> 263 us).  Casts whose stores all write whole
+  // lines (blocked scales, dim1 only) are as fast or faster rotated at every
+  // shape timed (16384 x 2048: 29.8 -> 28.0 us; 16384 x 16384 unchanged);
+  // the plain and grouped ones, whose partial scale lines merge in the L2 of
+  // the XCD running the neighbouring tiles, are slower rotated elsewhere
+  // (16384 x 16384: 185 against 193 us).
+  a.rotate = q0 == nullptr || blocked || (per % ct == 0 && (per / ct) % 32 == 0) ? 1u : 0u;
   a.ends = nullptr;
   a.groups = 0;
   a.out_starts = nullptr;
