@@ -496,6 +496,14 @@ __global__ __launch_bounds__(256) void cast_kernel(CastArgs a) {
       auto v = __builtin_amdgcn_raw_buffer_load_b128(xs, x_off, (int)(i * row_bytes), kLoadNT);
       d[i] = make_uint4(v[0], v[1], v[2], v[3]);
     }
+    if constexpr (MGRP) {
+      // A few groups: wave 0 (always on) reads the ends with scalar loads
+      // while its input loads are in flight, before its first store.  Read
+      // with vector loads after the stores, they would wait for every one of
+      // them: the vector memory counter counts stores too.
+      if (wave == 0 && a.groups <= kScalarTableGroups)
+        build_group_table_scalar(a.ends, a.groups, (int32_t)a.rows, kTileRows, table);
+    }
     {
       // Magnitudes once; row maxima of row pairs and column maxima from them.
       uint32_t rm[kLaneRows / 2];
@@ -570,7 +578,8 @@ __global__ __launch_bounds__(256) void cast_kernel(CastArgs a) {
 
   if constexpr (MGRP) {
     if (wave == 0) {
-      build_group_table(a.ends, a.groups, (int32_t)a.rows, kTileRows, table);
+      if (a.groups > kScalarTableGroups)
+        build_group_table(a.ends, a.groups, (int32_t)a.rows, kTileRows, table);
       if constexpr (KGRP)
         build_kstarts(table, a.groups, kstarts);
     }
