@@ -74,6 +74,23 @@ mx_status mx_cast_dim0_dim1(const void* x, int64_t rows, int64_t cols, uint8_t* 
     return MX_ERR_SHAPE;
   if (!aligned(x, 16) || (d0 && !aligned(q_row, 8)) || (d1 && !aligned(q_col, 16)))
     return MX_ERR_ALIGN;
+  // Where every 128-row band of both scale matrices fits one workgroup's
+  // LDS, the scales are written in the blocked layout, whose stores are whole
+  // lines, and then turned into the plain one in place (the same bytes): at
+  // 16384 x 16384, 162.5 + 11 us (177 us per call) against 182 us for the
+  // partial 1- and 4-byte scale runs of the direct kernel.
+  const bool via_blocked = rows % 128 == 0 && cols % 128 == 0 &&
+                           (!d0 || (cols / MX_BLOCK <= mx::kUnblockMaxCols && aligned(s_row, 16))) &&
+                           (!d1 || (rows / MX_BLOCK <= mx::kUnblockMaxCols && aligned(s_col, 16)));
+  if (via_blocked) {
+    hipError_t e = mx::launch_cast_any(static_cast<const uint16_t*>(x), rows, cols, rows, d0 ? q_row : nullptr,
+                                       d0 ? s_row : nullptr, d1 ? q_col : nullptr, d1 ? s_col : nullptr, true,
+                                       stream);
+    if (e == hipSuccess)
+      e = mx::launch_unblock_inplace(d0 ? s_row : nullptr, rows, cols / MX_BLOCK, d1 ? s_col : nullptr, cols,
+                                     rows / MX_BLOCK, stream);
+    return from_hip(e);
+  }
   return from_hip(mx::launch_cast_any(static_cast<const uint16_t*>(x), rows, cols, rows,
                                       d0 ? q_row : nullptr, d0 ? s_row : nullptr,
                                       d1 ? q_col : nullptr, d1 ? s_col : nullptr, false, stream));

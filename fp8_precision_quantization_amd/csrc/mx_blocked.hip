@@ -280,4 +280,89 @@ hipError_t launch_blocked_grouped(const uint8_t* s, int64_t rows, int64_t cols, 
   return launch_blocked(axis == 0 ? kModeMGroups : kModeKGroups, a, stream);
 }
 
+// The inverse map, in place: e8m0 scale matrices of R x C bytes (R % 128 ==
+// 0, C % 4 == 0, C <= kUnblockMaxCols) from the 128x4 blocked layout to the
+// plain row-major one.  A 128-row band occupies the same 128 * C bytes in
+// both layouts (in the blocked one as its C / 4 tiles, one after another), so
+// one workgroup per band reads the whole band with contiguous 16-byte loads,
+// regroups it in LDS and writes it back as contiguous rows.  Dword j of chunk
+// i of tile k is row i + 32 j, scale columns 4 k .. 4 k + 3.  Every load of a
+// band has returned (its value is in LDS) before the barrier, and only after
+// it does any thread of the workgroup store into the band.
+constexpr int kUnblockTiles = kUnblockMaxCols / 4;     // tiles per band, at most
+constexpr int kUnblockPitch = kUnblockTiles + 1;       // dwords per staged row (odd: no bank conflicts)
+constexpr int kUnblockThreads = 1024;                  // 16 waves share a band's latency
+constexpr int kUnblockChunks = kUnblockTiles * 32 / kUnblockThreads;   // 16-byte chunks per thread, at most
+constexpr int kUnblockDwords = kUnblockTiles * kTileRows / kUnblockThreads;   // dwords stored per thread, at most
+
+__global__ __launch_bounds__(kUnblockThreads) void unblock_kernel(uint8_t* m0, int64_t c0, int64_t bands0,
+                                                                  uint8_t* m1, int64_t c1) {
+  __shared__ uint32_t staged[kTileRows * kUnblockPitch];
+  int64_t band = blockIdx.x;
+  uint8_t* m = m0;
+  int64_t c = c0;
+  if (band >= bands0) {
+    band -= bands0;
+    m = m1;
+    c = c1;
+  }
+  const int tiles = (int)(c / 4);
+  const int chunks = tiles * 32;
+  uint8_t* base = m + band * kTileRows * c;
+  const int t = threadIdx.x;
+  uint4 v[kUnblockChunks];
+#pragma unroll
+  for (int n = 0; n < kUnblockChunks; ++n) {
+    const int q = t + kUnblockThreads * n;
+    if (q < chunks)
+      v[n] = *reinterpret_cast<const uint4*>(base + 16 * (int64_t)q);
+  }
+#pragma unroll
+  for (int n = 0; n < kUnblockChunks; ++n) {
+    const int q = t + kUnblockThreads * n;
+    if (q < chunks) {
+      const int k = q >> 5, i = q & 31;
+      staged[i * kUnblockPitch + k] = v[n].x;
+      staged[(i + 32) * kUnblockPitch + k] = v[n].y;
+      staged[(i + 64) * kUnblockPitch + k] = v[n].z;
+      staged[(i + 96) * kUnblockPitch + k] = v[n].w;
+    }
+  }
+  __syncthreads();
+  // plain dword d = r * tiles + k for d = t, t + 1024, ...; all LDS reads
+  // first, then the stores
+  uint32_t* out = reinterpret_cast<uint32_t*>(base);
+  const int total = tiles * kTileRows;
+  const int step_r = kUnblockThreads / tiles, step_k = kUnblockThreads % tiles;
+  int r = t / tiles, k = t % tiles;
+  uint32_t w[kUnblockDwords];
+#pragma unroll
+  for (int n = 0; n < kUnblockDwords; ++n) {
+    if (t + kUnblockThreads * n < total)
+      w[n] = staged[r * kUnblockPitch + k];
+    r += step_r;
+    k += step_k;
+    if (k >= tiles) {
+      k -= tiles;
+      ++r;
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < kUnblockDwords; ++n) {
+    const int d = t + kUnblockThreads * n;
+    if (d < total)
+      out[d] = w[n];
+  }
+}
+
+hipError_t launch_unblock_inplace(uint8_t* m0, int64_t r0, int64_t c0, uint8_t* m1, int64_t r1, int64_t c1,
+                                  hipStream_t stream) {
+  const int64_t b0 = m0 != nullptr ? r0 / kTileRows : 0;
+  const int64_t b1 = m1 != nullptr ? r1 / kTileRows : 0;
+  if (b0 + b1 == 0)
+    return hipSuccess;
+  hipLaunchKernelGGL(unblock_kernel, dim3((unsigned)(b0 + b1)), dim3(kUnblockThreads), 0, stream, m0, c0, b0, m1, c1);
+  return hipGetLastError();
+}
+
 }  // namespace mx

@@ -33,6 +33,13 @@ hipError_t launch_blocked_grouped(const uint8_t* s, int64_t rows, int64_t cols, 
                                   int32_t groups, int32_t axis, uint8_t* out, int64_t out_bytes,
                                   int64_t* out_starts, hipStream_t stream);
 
+// In place, blocked -> plain: scale matrices m0 (r0 x c0 bytes) and m1 (r1 x
+// c1), either may be null; rows multiples of 128, columns multiples of 4 and
+// at most kUnblockMaxCols, 16-byte aligned.
+constexpr int64_t kUnblockMaxCols = 512;
+hipError_t launch_unblock_inplace(uint8_t* m0, int64_t r0, int64_t c0, uint8_t* m1, int64_t r1, int64_t c1,
+                                  hipStream_t stream);
+
 // Row-wise fp8 cast.  vec: cols % 8 == 0, x 16-byte and q 8-byte aligned.
 hipError_t launch_rowwise(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* q, uint16_t* s, bool vec,
                           hipStream_t stream);

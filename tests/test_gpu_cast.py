@@ -70,6 +70,21 @@ def test_single_direction(oracle_mod, dim0, dim1):
     check_cast(oracle_mod, bits, dev, "single", dim0=dim0, dim1=dim1)
 
 
+# Rows and cols multiples of 128 with at most 512 scale columns in each
+# scale matrix: the scales are written in the blocked layout and converted
+# back to rows in place, one 128-row band per workgroup.  The last two shapes
+# sit just past that bound (direct path).
+VIA_BLOCKED = [(128, 128), (384, 640), (1152, 384), (128, 16384), (16384, 128), (256, 16512), (16512, 256)]
+
+
+@pytest.mark.parametrize("dim0,dim1", [(True, True), (True, False), (False, True)])
+@pytest.mark.parametrize("shape", VIA_BLOCKED)
+def test_scales_through_blocked_layout(oracle_mod, shape, dim0, dim1):
+    dev = device()
+    bits = workloads.special_values_bf16(shape, seed=[23, shape[0], shape[1]], p_special=0.001)
+    check_cast(oracle_mod, bits, dev, "%s dim0=%s dim1=%s" % (shape, dim0, dim1), dim0=dim0, dim1=dim1)
+
+
 def reachable_pairs(cols=1024):
     """Blocks that put every bf16 pattern against every finite scale byte it
     can meet: for scale byte b, one element is the largest magnitude with that
