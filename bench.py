@@ -360,6 +360,41 @@ def setup_square(dev, n=16384, fused=True):
     return step, step_bytes, timer, kern_bytes, kern_name, cpu_baseline, config
 
 
+def setup_square_plain(dev, n=16384):
+    """mx_cast_dim0_dim1 alone: both codes and both scale sets in the plain
+    row-major layout, one call per step (at this shape the call enqueues the
+    blocked-scale cast and the in-place conversion of its scales to rows)."""
+    log("generating %dx%d heavy-tailed bf16 input" % (n, n))
+    bits = workloads.heavy_tailed_rows(n, n, seed=2)
+    x = to_dev_bf16(bits, dev)
+    q0 = torch.empty((n, n), dtype=torch.uint8, device=dev)
+    q1 = torch.empty((n, n), dtype=torch.uint8, device=dev)
+    s0 = torch.empty((n, n // 32), dtype=torch.uint8, device=dev)
+    s1 = torch.empty((n, n // 32), dtype=torch.uint8, device=dev)
+    mx.mx_cast_dim0_dim1(x, out=(q0, s0, q1, s1), raw=True)
+    cast = c_call("mx_cast_dim0_dim1", x, n, n, q0, s0, q1, s1)
+    timer = Timer(whole_step=True)
+
+    def step():
+        with timer:
+            cast()
+
+    nb = cast_bytes(n, n)
+
+    def cpu_baseline():
+        def run(o):
+            return o.cast_dim0(bits) + o.cast_dim1(bits)
+
+        def compare(r):
+            return {"q_row": n_bad(q0, r[0]), "s_row": n_bad(s0, r[1]), "q_col": n_bad(q1, r[2]),
+                    "s_col": n_bad(s1, r[3])}
+        return oracle_leg(nb, "the whole %dx%d input (dim0+dim1 cast, plain scales)" % (n, n), run, compare)
+
+    config = {"workload": "mx_cast_dim0_dim1 %dx%d bf16 (heavy-tailed rows), plain row-major scales" % (n, n),
+              "rows": n, "cols": n, "block": 32, "elem": "e4m3", "scale": "e8m0"}
+    return step, nb, timer, nb, "cast dim0+dim1, plain scales (one call)", cpu_baseline, config
+
+
 def setup_square_3launch(dev):
     return setup_square(dev, fused=False)
 
@@ -897,6 +932,7 @@ def setup_copy(dev, nbytes=1 << 30):
 
 
 WORKLOADS = {"square16384": setup_square, "square16384_3launch": setup_square_3launch,
+             "square16384_plain": setup_square_plain,
              "moe16640": setup_moe, "moe16640_2launch": setup_moe_2launch, "kgroups": setup_kgroups, "rowwise16384": setup_rowwise,
              "tensorwise16384": setup_tensorwise, "moe16640_both": setup_moe_both,
              "moe16640_both_2launch": setup_moe_both_2launch, "gemm16640": setup_gemm, "ggemm16640": setup_ggemm, "kggemm16640": setup_kggemm,
