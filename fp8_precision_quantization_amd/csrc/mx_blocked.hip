@@ -23,6 +23,9 @@
 // grouped forms rebuild the group table (clamped ends, padded starts) in LDS
 // in every workgroup with one wave-wide scan, so the whole conversion is a
 // single launch with no host round trip.
+//
+// unblock_kernel (end of file) is the inverse map, in place, behind the
+// plain-scale cast.
 #include <type_traits>
 
 #include "mx_device.h"
