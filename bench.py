@@ -32,9 +32,10 @@ sets written in the 128x4 blocked layout by the same launch.  Other workloads
   ggemm16640 the same grouped along M (4 groups, per-group weights);
   kggemm16640  the weight-gradient GEMM grouped along K: 4 outputs of
              (8192, 5120), K = the 16640 tokens split in 4 groups;
-  cast_blocked, cast_grouped  the blocked-scale cast, or the cast with both
-             scale sets grouped (4 equal groups of rows), at any --rows
-             --cols (default 16384 x 16384; N(0,1) input drawn on the GPU);
+  cast_blocked, cast_grouped, cast_plain  the blocked-scale cast, the cast
+             with both scale sets grouped (4 equal groups of rows), or the
+             plain-scale cast, at any --rows --cols (default 16384 x 16384;
+             N(0,1) input drawn on the GPU);
   copy       a plain device-to-device copy of 1 GiB (counter calibration).
 
 Each workload's calls are validated once through the Python binding; the
@@ -878,10 +879,10 @@ def _device_normal_bf16(rows, cols, seed, dev):
     return torch.randn((rows, cols), generator=g, device=dev).to(torch.bfloat16)
 
 
-def setup_cast_shape(dev, rows=16384, cols=16384, grouped=False):
+def setup_cast_shape(dev, rows=16384, cols=16384, grouped=False, plain=False):
     """The dim0+dim1 cast at any shape (--rows, --cols), N(0,1) input drawn
-    on the device: blocked scales, or (grouped) 4 equal groups of rows with
-    both scale sets grouped."""
+    on the device: blocked scales, (grouped) 4 equal groups of rows with both
+    scale sets grouped, or (plain) plain row-major scales."""
     x = _device_normal_bf16(rows, cols, 7, dev)
     u8 = dict(dtype=torch.uint8, device=dev)
     q0 = torch.empty((rows, cols), **u8)
@@ -901,6 +902,14 @@ def setup_cast_shape(dev, rows=16384, cols=16384, grouped=False):
         nb = rows * cols * 4 + s0.numel() + s1.numel() + 16 * (g + 1)
         label = "mx_cast_dim0_dim1_grouped_blocked %dx%d bf16 N(0,1), 4 equal groups, both scale sets grouped"
         name = "cast dim0+dim1, M- and K-grouped scales"
+    elif plain:
+        s0 = torch.empty((rows, cols // 32), **u8)
+        s1 = torch.empty((cols, rows // 32), **u8)
+        mx.mx_cast_dim0_dim1(x, out=(q0, s0, q1, s1), raw=True)
+        call = c_call("mx_cast_dim0_dim1", x, rows, cols, q0, s0, q1, s1)
+        nb = cast_bytes(rows, cols)
+        label = "mx_cast_dim0_dim1 %dx%d bf16 N(0,1), plain row-major scales"
+        name = "cast dim0+dim1, plain scales (one call)"
     else:
         s0 = torch.empty((pad(rows, 128), pad(cols // 32, 4)), **u8)
         s1 = torch.empty((pad(cols, 128), pad(rows // 32, 4)), **u8)
@@ -938,7 +947,8 @@ WORKLOADS = {"square16384": setup_square, "square16384_3launch": setup_square_3l
              "moe16640_both_2launch": setup_moe_both_2launch, "gemm16640": setup_gemm, "ggemm16640": setup_ggemm, "kggemm16640": setup_kggemm,
              "experts16": setup_experts, "experts16_2launch": setup_experts_2launch, "copy": setup_copy,
              "cast_blocked": setup_cast_shape,
-             "cast_grouped": lambda dev, **kw: setup_cast_shape(dev, grouped=True, **kw)}
+             "cast_grouped": lambda dev, **kw: setup_cast_shape(dev, grouped=True, **kw),
+             "cast_plain": lambda dev, **kw: setup_cast_shape(dev, plain=True, **kw)}
 
 
 def main():
@@ -948,8 +958,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="square16384", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--rows", type=int, default=None, help="rows of the cast_blocked / cast_grouped workloads")
-    ap.add_argument("--cols", type=int, default=None, help="cols of the cast_blocked / cast_grouped workloads")
+    ap.add_argument("--rows", type=int, default=None, help="rows of the cast_blocked / cast_grouped / cast_plain workloads")
+    ap.add_argument("--cols", type=int, default=None, help="cols of the cast_blocked / cast_grouped / cast_plain workloads")
     ap.add_argument("--cold-launches", type=int, default=50,
                     help="steps timed one by one after cache-evicting traffic (0: skip)")
     args = ap.parse_args()
@@ -964,8 +974,9 @@ def main():
     mx.lib()
 
     shape = {k: v for k, v in (("rows", args.rows), ("cols", args.cols)) if v is not None}
-    if shape and args.workload not in ("cast_blocked", "cast_grouped"):
-        print("--rows / --cols apply to the cast_blocked and cast_grouped workloads only", file=sys.stderr)
+    if shape and args.workload not in ("cast_blocked", "cast_grouped", "cast_plain"):
+        print("--rows / --cols apply to the cast_blocked, cast_grouped and cast_plain workloads only",
+              file=sys.stderr)
         sys.exit(2)
     step, step_bytes, timer, kern_bytes, kern_name, cpu_fn, config = WORKLOADS[args.workload](dev, **shape)
     timer.reserve(args.warmup + args.steps)

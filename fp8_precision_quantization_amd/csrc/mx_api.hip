@@ -74,12 +74,15 @@ mx_status mx_cast_dim0_dim1(const void* x, int64_t rows, int64_t cols, uint8_t* 
     return MX_ERR_SHAPE;
   if (!aligned(x, 16) || (d0 && !aligned(q_row, 8)) || (d1 && !aligned(q_col, 16)))
     return MX_ERR_ALIGN;
-  // Where every 128-row band of both scale matrices fits one workgroup's
+  // On large, tall inputs whose 128-row scale bands all fit one workgroup's
   // LDS, the scales are written in the blocked layout, whose stores are whole
-  // lines, and then turned into the plain one in place (the same bytes): at
-  // 16384 x 16384, 162.5 + 11 us (177 us per call) against 182 us for the
-  // partial 1- and 4-byte scale runs of the direct kernel.
-  const bool via_blocked = rows % 128 == 0 && cols % 128 == 0 &&
+  // lines, and then turned into the plain one in place (the same bytes).
+  // Timed on MI355X against the direct kernel's partial 1- and 4-byte scale
+  // runs: 16384 x 16384 174 against 181 us, 16384 x 4096 55 against 61 us,
+  // 16384 x 8192 and 8192 x 16384 about even; 4096 x 16384 and every smaller
+  // input slower (the conversion's own ~5-11 us and second launch), hence
+  // the size bound.
+  const bool via_blocked = rows >= 16384 && cols >= 4096 && rows % 128 == 0 && cols % 128 == 0 &&
                            (!d0 || (cols / MX_BLOCK <= mx::kUnblockMaxCols && aligned(s_row, 16))) &&
                            (!d1 || (rows / MX_BLOCK <= mx::kUnblockMaxCols && aligned(s_col, 16)));
   if (via_blocked) {

@@ -70,11 +70,13 @@ def test_single_direction(oracle_mod, dim0, dim1):
     check_cast(oracle_mod, bits, dev, "single", dim0=dim0, dim1=dim1)
 
 
-# Rows and cols multiples of 128 with at most 512 scale columns in each
-# scale matrix: the scales are written in the blocked layout and converted
-# back to rows in place, one 128-row band per workgroup.  The last two shapes
-# sit just past that bound (direct path).
-VIA_BLOCKED = [(128, 128), (384, 640), (1152, 384), (128, 16384), (16384, 128), (256, 16512), (16512, 256)]
+# At least 16384 rows and 4096 cols, multiples of 128, at most 512 scale
+# columns in each scale matrix present: the scales are written in the blocked
+# layout and converted back to rows in place, one 128-row band per workgroup
+# (16384 x 16384 is covered by the full-size configuration test).  16512 rows
+# take that path for dim0 alone (their dim1 scale rows are too long);
+# 3968 columns sit just under the size bound (direct path).
+VIA_BLOCKED = [(16384, 4096), (16512, 4096), (16384, 3968)]
 
 
 @pytest.mark.parametrize("dim0,dim1", [(True, True), (True, False), (False, True)])
