@@ -693,11 +693,13 @@ static CastArgs cast_args(const uint16_t* x, int64_t rows, int64_t cols, int64_t
   // and (16 * 8192) x 5120: the dim0+dim1 cast with blocked scales favours
   // the widest groups, with plain scales somewhat taller ones (the tiles
   // that share a plain scale line then run together on one XCD), the
-  // dim1-only cast the tallest (all of its stores are col-major: an XCD
-  // walking whole column strips writes each output row's 128-byte pieces
-  // one after another; 353 us at (16 * 8192) x 5120 against 361 with 512
-  // and 371 with 256 row tiles).
-  a.row_group = q0 != nullptr ? (blocked ? kRowGroupBlocked : kRowGroupPlain) : kRowGroupDim1;
+  // dim1-only cast one segment's height (all of its stores are col-major: an
+  // XCD walking a segment's whole column strip writes each of its output rows
+  // from end to end, 128 bytes per tile; at (16 * 8192) x 5120, 64 row tiles
+  // 345 us against 352 with 32, 355 with 128, 353 with 1024 and 384 with 16).
+  a.row_group = q0 != nullptr ? (blocked ? kRowGroupBlocked : kRowGroupPlain)
+                              : (uint32_t)std::min<int64_t>(kRowGroupDim1,
+                                                            std::max<int64_t>(1, rows_per_seg / kTileRows));
   // With every XCD at the start of its piece, XCDs whose pieces begin a
   // multiple of 4 KiB apart in the col-major output (pieces of whole row
   // bands, per / ct row tiles of 128 bytes there, a multiple of 32) write it
