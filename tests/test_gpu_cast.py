@@ -87,6 +87,31 @@ def test_scales_through_blocked_layout(oracle_mod, shape, dim0, dim1):
     check_cast(oracle_mod, bits, dev, "%s dim0=%s dim1=%s" % (shape, dim0, dim1), dim0=dim0, dim1=dim1)
 
 
+def test_scales_off_16_byte_alignment(oracle_mod):
+    """Scale buffers 4 bytes past a 16-byte boundary at a shape that would
+    otherwise go through the blocked layout: the direct kernel writes them
+    (the plain scales carry no alignment requirement), and the bytes before
+    each buffer stay untouched."""
+    dev = device()
+    r, c = 16384, 4096
+    bits = workloads.special_values_bf16((r, c), seed=[29, r, c], p_special=0.001)
+    bufs = [sentinel((n + 4,), dev) for n in (r * (c // 32), c * (r // 32))]
+    s0 = bufs[0][4:].view(r, c // 32)
+    s1 = bufs[1][4:].view(c, r // 32)
+    assert s0.data_ptr() % 16 == 4 and s1.data_ptr() % 16 == 4
+    q0, q1 = sentinel((r, c), dev), sentinel((c, r), dev)
+    mx.mx_cast_dim0_dim1(to_dev_bf16(bits, dev), out=(q0, s0, q1, s1), raw=True)
+    torch.cuda.synchronize(dev)
+    r_q0, r_s0 = oracle_mod.cast_dim0(bits)
+    r_q1, r_s1 = oracle_mod.cast_dim1(bits)
+    assert_bytes_equal(host(q0), r_q0, "off-alignment q_row")
+    assert_bytes_equal(host(s0), r_s0, "off-alignment s_row")
+    assert_bytes_equal(host(q1), r_q1, "off-alignment q_col")
+    assert_bytes_equal(host(s1), r_s1, "off-alignment s_col")
+    for b in bufs:
+        assert np.all(host(b[:4]) == 0xCD), "bytes before a scale buffer written"
+
+
 def reachable_pairs(cols=1024):
     """Blocks that put every bf16 pattern against every finite scale byte it
     can meet: for scale byte b, one element is the largest magnitude with that
