@@ -6,6 +6,7 @@ import torch
 
 import fp8_precision_quantization_amd as mx
 from fp8_precision_quantization_amd import workloads
+from tests import sweep_blocks as sb
 from tests.gpu_util import assert_bytes_equal, device, host, sentinel, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
@@ -114,28 +115,9 @@ def test_scales_off_16_byte_alignment(oracle_mod):
 
 def reachable_pairs(cols=1024):
     """Blocks that put every bf16 pattern against every finite scale byte it
-    can meet: for scale byte b, one element is the largest magnitude with that
-    byte, ((b + 8) << 7) | 0x7F, and the other 31 slots run through every
-    magnitude up to it, with both signs.  The anchor's slot rotates."""
-    blocks = []
-    for b in range(0, 247):
-        anchor = ((b + 8) << 7) | 0x7F
-        mags = np.arange(anchor + 1, dtype=np.uint32)
-        vals = np.concatenate([mags, mags | 0x8000]).astype(np.uint16)
-        nb = -(-vals.size // 31)
-        vals = np.concatenate([vals, np.zeros(nb * 31 - vals.size, np.uint16)]).reshape(nb, 31)
-        blk = np.empty((nb, 32), np.uint16)
-        pos = np.arange(nb) % 32
-        for p in range(32):
-            sel = pos == p
-            blk[sel, :p] = vals[sel, :p]
-            blk[sel, p] = anchor
-            blk[sel, p + 1:] = vals[sel, p:]
-        blocks.append(blk)
-    flat = np.concatenate(blocks).reshape(-1)
-    per = cols * 32
-    flat = np.concatenate([flat, np.zeros(-flat.size % per, np.uint16)])
-    return flat.reshape(-1, cols)
+    can meet (sweep_blocks.finite_pair_blocks), with no +-Inf or NaN, so that
+    every wave takes the kernels' finite path."""
+    return sb.blocks_to_matrix(sb.finite_pair_blocks(), cols)
 
 
 def test_exhaustive_reachable_pairs(oracle_mod):
