@@ -13,7 +13,9 @@ constexpr int64_t kMaxExtent = (int64_t)1 << 40;  // per-dimension bound, keeps 
 // The cast kernels address 32 rows of a row-major matrix from one scalar base
 // with 32-bit row offsets: 32 * cols * 2 bytes must stay below 2^31.
 constexpr int64_t kMaxCastCols = (int64_t)1 << 25;
-constexpr int64_t kMaxGridBlocks = INT_MAX;
+// The dispatch packet holds the grid size in work-items as a 32-bit field, and
+// every launch checked against this bound has 256 threads per workgroup.
+constexpr int64_t kMaxGridBlocks = (int64_t)UINT32_MAX / 256;
 constexpr int64_t kMaxRowwiseCols = (int64_t)1 << 30;
 // The GEMM addresses a wave's 64 operand rows from one base with 32-bit
 // offsets: 64 * k bytes must stay below 2^31.

@@ -461,7 +461,8 @@ __global__ __launch_bounds__(256) void cast_kernel(CastArgs a) {
   static_assert(!KGRP || (MGRP && DIM1 && !BLK), "K-grouped dim1 scales come with the M-grouped cast");
   __shared__ std::conditional_t<DIM1, Stage, NoStage> stage;
   // the tile's dim0 scales: two blocked tiles (BLK) or a plain image (MGRP)
-  __shared__ uint8_t s0_blk[(DIM0 && (BLK || MGRP)) ? 2 * 512 : 1];
+  // read back as 16- and 8-byte words
+  __shared__ __attribute__((aligned(16))) uint8_t s0_blk[(DIM0 && (BLK || MGRP)) ? 2 * 512 : 1];
   __shared__ std::conditional_t<MGRP, GroupTable, NoTable> table;
   __shared__ std::conditional_t<KGRP, KStarts, NoKStarts> kstarts;
 

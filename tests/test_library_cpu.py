@@ -168,6 +168,22 @@ def test_rowwise_validation(lib):
     assert f(None, 4, 0, None, None, None) == OK
 
 
+def test_grid_size_bound(lib):
+    """A launch holds at most 2^32 - 1 work-items (workgroups x 256): calls
+    whose grid would exceed that are rejected on the host as shapes, before
+    any HIP call, instead of failing at the launch."""
+    rw = lib.mx_quantize_fp8_rowwise
+    # one workgroup per row (cols % 8 != 0): 2^24 rows is one too many
+    assert rw(P, 1 << 24, 4, P, P, None) == ERR_SHAPE
+    # four rows per workgroup (8 columns, aligned)
+    assert rw(P, (1 << 26) + 4, 8, P, P, None) == ERR_SHAPE
+    # the MX cast: 128 x 256 tiles, 2^31 rows of 32 columns = 2^24 tiles
+    c = lib.mx_cast_dim0_dim1
+    assert c(P, 1 << 31, 32, P, P, P, P, None) == ERR_SHAPE
+    assert lib.mx_cast_dim0_dim1_blocked(P, 1 << 31, 32, P, P, P, P, None) == ERR_SHAPE
+    assert lib.mx_cast_dim1_3d(P, 1 << 10, 1 << 21, 32, P, P, None) == ERR_SHAPE
+
+
 def test_tensorwise_validation(lib):
     ws = lib.mx_tensorwise_workspace_bytes
     assert ws(-1) == -1 and ws((1 << 40) + 1) == -1
