@@ -21,6 +21,7 @@ from ._binding import (  # noqa: F401
     mx_kgrouped_gemm_mxfp8,
     mx_quantize_fp8_rowwise,
     mx_quantize_fp8_tensorwise,
+    mx_quantize_fp8_tensorwise_noalloc,
     mx_scales_to_blocked,
     mx_scales_to_blocked_grouped,
     mx_tensorwise_workspace_bytes,

@@ -39,6 +39,7 @@ SIGNATURES = {
     "mx_quantize_fp8_rowwise": ([_vp, _i64, _i64, _vp, _vp, _vp], ctypes.c_int),
     "mx_tensorwise_workspace_bytes": ([_i64], _i64),
     "mx_quantize_fp8_tensorwise": ([_vp, _i64, _vp, _vp, _vp, _i64, _vp], ctypes.c_int),
+    "mx_quantize_fp8_tensorwise_noalloc": ([_vp, _i64, _vp, _vp, _vp], ctypes.c_int),
     "mx_gemm_mxfp8": ([_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _i32, _vp], ctypes.c_int),
     "mx_grouped_gemm_mxfp8": ([_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _i32, _vp], ctypes.c_int),
     "mx_kgrouped_gemm_mxfp8": ([_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _i32, _vp], ctypes.c_int),
@@ -317,6 +318,30 @@ def mx_quantize_fp8_tensorwise(x, out=None, workspace=None, raw: bool = False):
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(lib().mx_quantize_fp8_tensorwise(_ptr(x), n, _ptr(q), _ptr(s), _ptr(workspace), ws_bytes,
                                             _stream(x.device)), "mx_quantize_fp8_tensorwise")
+    if raw:
+        return q, s.view(torch.int16)
+    return q.view(torch.float8_e4m3fn), s.view(torch.bfloat16)
+
+
+def mx_quantize_fp8_tensorwise_noalloc(x, out=None, raw: bool = False):
+    """mx_quantize_fp8_tensorwise with the block amaxes in the library's
+    static per-GPU scratch instead of a workspace (nothing is allocated when
+    `out` is given).  Calls that overlap on one GPU race."""
+    if not isinstance(x, torch.Tensor) or not x.is_cuda or x.dtype != torch.bfloat16:
+        raise ValueError("x must be a bfloat16 CUDA (HIP) tensor")
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    o = out if out is not None else (None, None)
+    q = _out(o[0], tuple(x.shape), x.device, "q")
+    if o[1] is None:
+        s = torch.empty(1, dtype=torch.bfloat16, device=x.device)
+    else:
+        s = o[1]
+        if (s.dtype not in (torch.bfloat16, torch.int16) or s.numel() != 1 or not s.is_contiguous()
+                or s.device != x.device):
+            raise ValueError("scale must be a one-element bf16 or int16 tensor on %s" % x.device)
+    _check(lib().mx_quantize_fp8_tensorwise_noalloc(_ptr(x), x.numel(), _ptr(q), _ptr(s), _stream(x.device)),
+           "mx_quantize_fp8_tensorwise_noalloc")
     if raw:
         return q, s.view(torch.int16)
     return q.view(torch.float8_e4m3fn), s.view(torch.bfloat16)

@@ -343,6 +343,27 @@ mx_status mx_quantize_fp8_tensorwise(const void* x, int64_t n, uint8_t* q, uint1
                                         static_cast<uint32_t*>(workspace), vec, stream));
 }
 
+mx_status mx_quantize_fp8_tensorwise_noalloc(const void* x, int64_t n, uint8_t* q, uint16_t* scale,
+                                             hipStream_t stream) {
+  if (n < 0 || n > kMaxExtent)
+    return MX_ERR_SHAPE;
+  if (n == 0)
+    return MX_OK;  // nothing to read or write; the pointers may be NULL
+  if (x == nullptr || q == nullptr || scale == nullptr)
+    return MX_ERR_NULL;
+  if (mx_tensorwise_workspace_bytes(n) > mx::tensorwise_scratch_bytes())
+    return MX_ERR_WORKSPACE;
+  if (!aligned(x, 2) || !aligned(scale, 2))
+    return MX_ERR_ALIGN;
+  const bool vec = aligned(x, 16) && aligned(q, 8);
+  if (mx::tensorwise_cast_blocks(n, vec) > kMaxGridBlocks)
+    return MX_ERR_SHAPE;
+  uint32_t* partial = nullptr;
+  if (mx::tensorwise_scratch(&partial) != hipSuccess)
+    return MX_ERR_HIP;
+  return from_hip(mx::launch_tensorwise(static_cast<const uint16_t*>(x), n, q, scale, partial, vec, stream));
+}
+
 mx_status mx_gemm_mxfp8(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, const uint8_t* sb, int64_t m,
                         int64_t n, int64_t k, void* c, int32_t c_bf16, hipStream_t stream) {
   const mx_status st = check_gemm(qa, sa, qb, sb, m, n, k, c, c_bf16);

@@ -45,11 +45,15 @@ hipError_t launch_rowwise(const uint16_t* x, int64_t rows, int64_t cols, uint8_t
                           hipStream_t stream);
 int64_t rowwise_grid_blocks(int64_t rows, int64_t cols, bool vec);
 
-// Tensor-wise fp8 cast (two launches); partial holds tensorwise_partials(n)
+// Tensor-wise fp8 cast (three launches); partial holds tensorwise_partials(n)
 // words.  vec: x 16-byte and q 8-byte aligned.
 hipError_t launch_tensorwise(const uint16_t* x, int64_t n, uint8_t* q, uint16_t* scale, uint32_t* partial,
                              bool vec, hipStream_t stream);
 int64_t tensorwise_partials(int64_t n);
+// The allocation-free variant's per-device scratch (the device address of a
+// static __device__ array, looked up on the current device) and its size.
+hipError_t tensorwise_scratch(uint32_t** out);
+int64_t tensorwise_scratch_bytes();
 int64_t tensorwise_cast_blocks(int64_t n, bool vec);
 
 // MX-scaled GEMM, c fp32 or bf16; modes: 0 dense, 1 grouped along M, 2 grouped

@@ -27,6 +27,8 @@
 // or codes are not 16- / 8-byte aligned is handled element by element with
 // the same three steps.  A tail of n % 8 elements after the last whole chunk
 // belongs to workgroup 0 of steps 1 and 3.
+#include <mutex>
+
 #include "mx_fp8.h"
 #include "mxcast.h"
 #include "mx_launch.h"
@@ -60,6 +62,38 @@ static TwPlan tw_plan(int64_t n, bool vec) {
 }
 
 int64_t tensorwise_partials(int64_t n) { return tw_plan(n, false).spans; }
+
+// Block amaxes of the allocation-free entry point: one array per GPU for the
+// life of the process, big enough for the largest plan (kTwMaxSpans words).
+// Host code never passes the array's name to a kernel (on the host it is a
+// stand-in, not the device address): tensorwise_scratch looks the address
+// up once per device, with that device current, and hands that out.
+static __device__ __align__(256) uint32_t scratch[kTwMaxSpans];
+
+constexpr int kScratchDevices = 64;
+static std::mutex g_scratch_mu;
+static uint32_t* g_scratch_ptr[kScratchDevices];
+
+int64_t tensorwise_scratch_bytes() { return (int64_t)sizeof(scratch); }
+
+hipError_t tensorwise_scratch(uint32_t** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess)
+    return e;
+  if (dev < 0 || dev >= kScratchDevices)
+    return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess)
+      return e;
+    g_scratch_ptr[dev] = static_cast<uint32_t*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 // Max over the 256 threads of a workgroup (every thread gets it).
 __device__ __forceinline__ uint32_t group_max(uint32_t m, uint32_t* lds4) {

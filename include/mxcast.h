@@ -313,7 +313,7 @@ MX_API mx_status mx_quantize_fp8_rowwise(const void* x, int64_t rows, int64_t co
  *              block amaxes between the two launches, needs no clearing and
  *              must not be used by another call until this one has run.
  * n < 0 or n > 2^40 -> MX_ERR_SHAPE; n == 0 writes nothing; a workspace
- * smaller than required -> MX_ERR_WORKSPACE.  Two kernels are enqueued; the
+ * smaller than required -> MX_ERR_WORKSPACE.  Three kernels are enqueued; the
  * input is read twice (the second time partly from the memory-side cache).
  * Fastest with x 16-byte and q 8-byte aligned.
  */
@@ -321,6 +321,25 @@ MX_API int64_t mx_tensorwise_workspace_bytes(int64_t n);
 MX_API mx_status mx_quantize_fp8_tensorwise(const void* x, int64_t n, uint8_t* q, uint16_t* scale,
                                             void* workspace, int64_t workspace_bytes,
                                             hipStream_t stream);
+
+/*
+ * mx_quantize_fp8_tensorwise without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same arguments, rule, kernels and
+ * results; the block amaxes live in a static device array of the library
+ * (8 KiB, 2048 words: enough for every n <= 2^40), one per GPU, held until
+ * the process ends.  The call allocates nothing; its first call on a device
+ * looks the array's address up (hipGetSymbolAddress) with that device
+ * current, so `stream` must belong to the current device.  Every call on a
+ * GPU shares that GPU's array: calls that overlap on one GPU (two streams,
+ * or two host threads) race and may return a wrong scale; serialise them.
+ * The array needs no clearing (each call writes every word it reads).
+ * Errors as mx_quantize_fp8_tensorwise; MX_ERR_WORKSPACE if n needed more
+ * than the array holds (unreachable for n <= 2^40); MX_ERR_HIP if the
+ * address lookup fails.
+ */
+MX_API mx_status mx_quantize_fp8_tensorwise_noalloc(const void* x, int64_t n, uint8_t* q, uint16_t* scale,
+                                                    hipStream_t stream);
 
 /*
  * MX-scaled GEMM, the consumer of the dim0 casts ("[mxfp8 moe training] add

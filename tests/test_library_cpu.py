@@ -36,6 +36,7 @@ def test_exports_every_declared_symbol(lib):
                           "mx_cast_dim0_dim1_mgrouped", "mx_cast_dim0_dim1_grouped_blocked",
                           "mx_cast_dim1_3d", "mx_cast_dim1_3d_blocked", "mx_quantize_fp8_rowwise",
                           "mx_tensorwise_workspace_bytes", "mx_quantize_fp8_tensorwise",
+                          "mx_quantize_fp8_tensorwise_noalloc",
                           "mx_gemm_mxfp8", "mx_grouped_gemm_mxfp8", "mx_kgrouped_gemm_mxfp8",
                           "mx_blocked_bytes", "mx_scales_to_blocked",
                           "mx_blocked_grouped_bytes", "mx_scales_to_blocked_grouped"}
@@ -200,6 +201,18 @@ def test_tensorwise_validation(lib):
     assert f(P, 64, P, P_ODD, P, 64, None) == ERR_ALIGN
     assert f(P, 64, P, P, ctypes.c_void_p(0x10002), 64, None) == ERR_ALIGN
     assert lib.mx_status_string(ERR_WORKSPACE) == b"the workspace is smaller than required"
+
+
+def test_tensorwise_noalloc_validation(lib):
+    f = lib.mx_quantize_fp8_tensorwise_noalloc
+    assert f(P, -1, P, P, None) == ERR_SHAPE
+    assert f(P, (1 << 40) + 1, P, P, None) == ERR_SHAPE
+    assert f(None, 0, None, None, None) == OK
+    assert f(None, 64, P, P, None) == ERR_NULL
+    assert f(P, 64, None, P, None) == ERR_NULL
+    assert f(P, 64, P, None, None) == ERR_NULL
+    assert f(P_ODD, 64, P, P, None) == ERR_ALIGN
+    assert f(P, 64, P, P_ODD, None) == ERR_ALIGN
 
 
 def test_blocked_sizes_match_oracle(lib, oracle_mod):

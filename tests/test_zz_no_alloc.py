@@ -1,0 +1,84 @@
+"""The allocation-free tensor-wise fp8 cast (mx_quantize_fp8_tensorwise_noalloc,
+block amaxes in the library's static per-GPU scratch) against the entry point
+that takes a workspace, called through the C ABI: two calls in a row, the
+second on a smaller input (so the scratch still holds more block amaxes from
+the first, larger ones, which the second must not read), then a third on an
+unaligned view.  Codes and scale must be byte-identical to the workspace
+entry point's and to the CPU oracle's."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_precision_quantization_amd as mx
+from fp8_precision_quantization_amd import workloads
+from tests.gpu_util import assert_bytes_equal, device, host, sentinel, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def _p(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _spread(n, seed, log2_scale):
+    """N(0,1) * 2^k, k drawn per 1000 elements, times 2^log2_scale."""
+    rng = np.random.default_rng(seed)
+    a = rng.standard_normal(n, dtype=np.float32)
+    k = np.repeat(rng.integers(-20, 6, size=n // 1000 + 1), 1000)[:n] + log2_scale
+    return workloads.bf16_bits((a * np.exp2(k)).astype(np.float32))
+
+
+def _outs(n, dev, fill):
+    return sentinel((n,), dev, fill), torch.full((1,), 0x5A5A, dtype=torch.int16, device=dev)
+
+
+def _scale_bits(s):
+    return int(s.cpu().numpy().view(np.uint16)[0])
+
+
+def test_noalloc_matches_workspace_entry_point(oracle_mod):
+    dev = device()
+    lib = mx.lib()
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    # the first input's block amaxes all exceed the second's amax
+    big = _spread(40_000_003, seed=1, log2_scale=12)
+    small = _spread(100_003, seed=2, log2_scale=0)
+    xs = [to_dev_bf16(b, dev) for b in (big, small)]
+    # a third call on the second input one element in (2-byte aligned only)
+    pad = torch.empty(small.size + 1, dtype=torch.bfloat16, device=dev)
+    pad[1:] = xs[1]
+    cases = [(xs[0], big.size, big), (xs[1], small.size, small), (pad[1:], small.size, small)]
+    noalloc = []
+    for x, n, _ in cases:
+        q, s = _outs(n, dev, 0xCD)
+        assert lib.mx_quantize_fp8_tensorwise_noalloc(_p(x), n, _p(q), _p(s), stream) == 0
+        noalloc.append((q, s))
+    with_ws = []
+    for x, n, _ in cases:
+        q, s = _outs(n, dev, 0x33)
+        ws = torch.empty(max(lib.mx_tensorwise_workspace_bytes(n), 4), dtype=torch.uint8, device=dev)
+        assert lib.mx_quantize_fp8_tensorwise(_p(x), n, _p(q), _p(s), _p(ws), ws.numel(), stream) == 0
+        with_ws.append((q, s))
+    torch.cuda.synchronize(dev)
+    for i, ((_, n, bits), (qa, sa), (qb, sb)) in enumerate(zip(cases, noalloc, with_ws)):
+        r_q, r_s = oracle_mod.quantize_fp8_tensorwise(bits)
+        assert _scale_bits(sa) == _scale_bits(sb) == r_s, (i, hex(_scale_bits(sa)), hex(_scale_bits(sb)), hex(r_s))
+        assert_bytes_equal(host(qa), host(qb), "call %d: no-alloc q vs workspace q" % i)
+        assert_bytes_equal(host(qa), r_q, "call %d: no-alloc q vs oracle" % i)
+    # the second input's scale differs from the first's: a stale block amax
+    # read by the second call would have shown
+    assert _scale_bits(noalloc[0][1]) != _scale_bits(noalloc[1][1])
+
+
+def test_noalloc_binding_and_empty_input(oracle_mod):
+    dev = device()
+    bits = _spread(1 << 16, seed=3, log2_scale=-3)
+    q, s = mx.mx_quantize_fp8_tensorwise_noalloc(to_dev_bf16(bits, dev), raw=True)
+    torch.cuda.synchronize(dev)
+    r_q, r_s = oracle_mod.quantize_fp8_tensorwise(bits)
+    assert int(s.cpu().numpy().view(np.uint16)[0]) == r_s
+    assert_bytes_equal(host(q), r_q, "binding q")
+    q0, _ = mx.mx_quantize_fp8_tensorwise_noalloc(torch.empty(0, dtype=torch.bfloat16, device=dev), raw=True)
+    assert q0.numel() == 0
