@@ -46,7 +46,7 @@ mx_status check_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, co
 
 extern "C" {
 
-const char* mx_status_string(mx_status status) {
+const char* mx_status_string(int status) {
   switch (status) {
     case MX_OK: return "ok";
     case MX_ERR_NULL: return "a required pointer is NULL";
@@ -243,7 +243,10 @@ int64_t mx_blocked_bytes(int64_t batch, int64_t rows, int64_t cols) {
   if (batch < 0 || rows < 0 || cols < 0 || batch > kMaxExtent || rows > kMaxExtent ||
       cols > kMaxExtent)
     return -1;
-  const int64_t per = round_up(rows, 128) * round_up(cols, 4);
+  const int64_t r = round_up(rows, 128), c = round_up(cols, 4);
+  if (c > 0 && r > INT64_MAX / c)
+    return -1;
+  const int64_t per = r * c;
   if (per > 0 && batch > INT64_MAX / per)
     return -1;
   return batch * per;
@@ -270,7 +273,8 @@ int64_t mx_blocked_grouped_bytes(int64_t rows, int64_t cols, int32_t num_groups,
   if (rows < 0 || cols < 0 || num_groups < 1 || num_groups > MX_MAX_GROUPS ||
       (group_axis != 0 && group_axis != 1))
     return -1;
-  if (rows + 128 * (int64_t)num_groups >= INT_MAX || cols + 4 * (int64_t)num_groups >= INT_MAX)
+  if (rows >= INT_MAX || cols >= INT_MAX || rows + 128 * (int64_t)num_groups >= INT_MAX ||
+      cols + 4 * (int64_t)num_groups >= INT_MAX)
     return -1;
   if (group_axis == 0)
     return (rows + 128 * (int64_t)num_groups) * round_up(cols, 4);
@@ -283,7 +287,7 @@ mx_status mx_scales_to_blocked_grouped(const uint8_t* s, int64_t rows, int64_t c
                                        int64_t* out_group_starts, hipStream_t stream) {
   if (num_groups < 1 || num_groups > MX_MAX_GROUPS || (group_axis != 0 && group_axis != 1))
     return MX_ERR_GROUPS;
-  if (rows < 0 || cols < 0 || rows + 128 * (int64_t)num_groups >= INT_MAX ||
+  if (rows < 0 || cols < 0 || rows >= INT_MAX || cols >= INT_MAX || rows + 128 * (int64_t)num_groups >= INT_MAX ||
       cols + 4 * (int64_t)num_groups >= INT_MAX)
     return MX_ERR_SHAPE;
   const int64_t bytes = mx_blocked_grouped_bytes(rows, cols, num_groups, group_axis);

@@ -42,9 +42,10 @@
  * Conventions for every call below:
  *  - All array arguments are DEVICE pointers, contiguous, row-major.
  *  - The caller owns every buffer (scratch included) and the stream.  The
- *    library allocates nothing, keeps no state, never synchronises and never reads device
+ *    library allocates nothing, never synchronises and never reads device
  *    memory from the host; all work is enqueued on `stream` (0 = the null
- *    stream) and runs asynchronously.
+ *    stream) and runs asynchronously.  It keeps no state, except the
+ *    per-GPU scratch array of mx_quantize_fp8_tensorwise_noalloc.
  *  - Arguments are validated on the host before any HIP call; a rejected
  *    call enqueues nothing.  A launch failure reported by the HIP runtime
  *    returns MX_ERR_HIP.
@@ -81,8 +82,9 @@ typedef enum {
 #define MX_BLOCK 32          /* elements per scale block                  */
 #define MX_MAX_GROUPS 1024   /* groups accepted by the grouped layout     */
 
-/* Static text for a status code. */
-MX_API const char* mx_status_string(mx_status status);
+/* Static text for a status code (any int: values that are not an mx_status
+ * give "unknown status"). */
+MX_API const char* mx_status_string(int status);
 
 /*
  * bf16 -> MXFP8 along dim0 and dim1 from one read of the input.

@@ -169,6 +169,18 @@ def test_rowwise_validation(lib):
     assert f(None, 4, 0, None, None, None) == OK
 
 
+def test_size_helpers_at_extremes(lib):
+    """No overflow in the size helpers: products past int64 and sums past
+    2^31 are reported as -1 (the sanitizer build checks the arithmetic)."""
+    big = (1 << 63) - 1
+    assert lib.mx_blocked_bytes(1, 1 << 40, 1 << 40) == -1
+    assert lib.mx_blocked_bytes(1, 1 << 30, 1 << 30) == (1 << 60)
+    assert lib.mx_blocked_grouped_bytes(big, 4, 1, 0) == -1
+    assert lib.mx_blocked_grouped_bytes(4, big, 1, 1) == -1
+    assert lib.mx_scales_to_blocked_grouped(P, big, 4, P, 1, 0, P, P, None) == ERR_SHAPE
+    assert lib.mx_scales_to_blocked_grouped(P, 4, big, P, 1, 1, P, P, None) == ERR_SHAPE
+
+
 def test_grid_size_bound(lib):
     """A launch holds at most 2^32 - 1 work-items (workgroups x 256): calls
     whose grid would exceed that are rejected on the host as shapes, before
