@@ -42,6 +42,13 @@ Each workload's calls are validated once through the Python binding; the
 timed loop then calls the same C-ABI entry points with their arguments
 marshalled in advance, so the host keeps ahead of the GPU.
 
+The default run also measures, before the headline's warm-up, the other
+workloads of the hot path (the `configs` object: the plain-scale call
+mx_cast_dim0_dim1 at 16384 x 16384, the MoE casts with M-grouped and with
+both scale sets grouped, the three K-grouped layouts and the 3D expert cast;
+each its back-to-back mean over 100 launches and its cold-cache median over
+20; --no-extras skips them).
+
 Prints exactly one JSON line on stdout; progress goes to stderr.  The
 `roofline` object is for the dominant kernel (the cast): algorithmic bytes per
 launch divided by its average duration from HIP events recorded on the stream
@@ -278,10 +285,21 @@ def n_bad(gpu, ref):
 # --------------------------------------------------------------------------
 # workloads
 # --------------------------------------------------------------------------
+_SQUARE = {}
+
+
+def square_input(dev, n=16384):
+    """The heavy-tailed (n, n) input (host bits and device copy), drawn once
+    per process and shared by the workloads that cast it."""
+    if n not in _SQUARE:
+        log("generating %dx%d heavy-tailed bf16 input" % (n, n))
+        bits = workloads.heavy_tailed_rows(n, n, seed=2)
+        _SQUARE[n] = (bits, to_dev_bf16(bits, dev))
+    return _SQUARE[n]
+
+
 def setup_square(dev, n=16384, fused=True):
-    log("generating %dx%d heavy-tailed bf16 input" % (n, n))
-    bits = workloads.heavy_tailed_rows(n, n, seed=2)
-    x = to_dev_bf16(bits, dev)
+    bits, x = square_input(dev, n)
     q0 = torch.empty((n, n), dtype=torch.uint8, device=dev)
     q1 = torch.empty((n, n), dtype=torch.uint8, device=dev)
     b0 = torch.empty((pad(n, 128), pad(n // 32, 4)), dtype=torch.uint8, device=dev)
@@ -365,9 +383,7 @@ def setup_square_plain(dev, n=16384):
     """mx_cast_dim0_dim1 alone: both codes and both scale sets in the plain
     row-major layout, one call per step (at this shape the call enqueues the
     blocked-scale cast and the in-place conversion of its scales to rows)."""
-    log("generating %dx%d heavy-tailed bf16 input" % (n, n))
-    bits = workloads.heavy_tailed_rows(n, n, seed=2)
-    x = to_dev_bf16(bits, dev)
+    bits, x = square_input(dev, n)
     q0 = torch.empty((n, n), dtype=torch.uint8, device=dev)
     q1 = torch.empty((n, n), dtype=torch.uint8, device=dev)
     s0 = torch.empty((n, n // 32), dtype=torch.uint8, device=dev)
@@ -583,11 +599,29 @@ def setup_kgroups(dev):
     return step, nb, timer, nb, "K-grouped layouts (three launches)", cpu_baseline, config
 
 
-def setup_experts(dev, experts=16, n=8192, k=5120, fused=True):
-    log("generating (%d, %d, %d) expert weights" % (experts, n, k))
+def device_expert_weights(experts, n, k, dev, seed=5):
+    """(experts, n, k) bf16 drawn on the device with the expert-weight recipe
+    (N(0, 0.02^2), a seeded 1% of the elements times 100): the same
+    distribution as workloads.expert_weight, other values (torch's device
+    generator), in a fraction of the host's time."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
     w = torch.empty((experts, n, k), dtype=torch.bfloat16, device=dev)
     for e in range(experts):
-        w[e] = to_dev_bf16(workloads.expert_weight(e, n, k), dev)
+        a = torch.randn((n, k), generator=g, device=dev) * 0.02
+        a = torch.where(torch.rand((n, k), generator=g, device=dev) < 0.01, a * 100.0, a)
+        w[e] = a.to(torch.bfloat16)
+    return w
+
+
+def setup_experts(dev, experts=16, n=8192, k=5120, fused=True, device_inputs=False):
+    if device_inputs:
+        w = device_expert_weights(experts, n, k, dev)
+    else:
+        log("generating (%d, %d, %d) expert weights" % (experts, n, k))
+        w = torch.empty((experts, n, k), dtype=torch.bfloat16, device=dev)
+        for e in range(experts):
+            w[e] = to_dev_bf16(workloads.expert_weight(e, n, k), dev)
     q = torch.empty((experts, k, n), dtype=torch.uint8, device=dev)
     out = torch.empty((experts, pad(k, 128), pad(n // 32, 4)), dtype=torch.uint8, device=dev)
     timer = Timer(whole_step=fused)
@@ -635,9 +669,12 @@ def setup_experts(dev, experts=16, n=8192, k=5120, fused=True):
         per_expert = nb // experts
         return oracle_leg(per_expert * sample, "the first %d of the %d experts (dim1 cast and blocked scales of "
                           "each (%d, %d) expert)" % (sample, experts, n, k), run, compare)
-    config = {"workload": "%s (%d, %d, %d) bf16 + per-expert blocked scale layout%s"
+    if device_inputs:
+        cpu_baseline = None
+    config = {"workload": "%s (%d, %d, %d) bf16 + per-expert blocked scale layout%s%s"
                           % ("mx_cast_dim1_3d_blocked" if fused else "mx_cast_dim1_3d", experts, n, k,
-                             "" if fused else " by mx_scales_to_blocked"),
+                             "" if fused else " by mx_scales_to_blocked",
+                             " (weights drawn on the device)" if device_inputs else ""),
               "experts": experts, "n": n, "k": k,
               "metric": "achieved HBM GB/s (% of MI355X peak) for the bf16->MXFP8 dim1 cast of 3D expert weights"}
     return step, nb, timer, cb, name, cpu_baseline, config
@@ -648,9 +685,7 @@ def setup_experts_2launch(dev):
 
 
 def setup_rowwise(dev, n=16384):
-    log("generating %dx%d heavy-tailed bf16 input" % (n, n))
-    bits = workloads.heavy_tailed_rows(n, n, seed=2)
-    x = to_dev_bf16(bits, dev)
+    bits, x = square_input(dev, n)
     q = torch.empty((n, n), dtype=torch.uint8, device=dev)
     s = torch.empty(n, dtype=torch.int16, device=dev)
     timer = Timer(whole_step=True)
@@ -683,9 +718,7 @@ def setup_rowwise(dev, n=16384):
 
 
 def setup_tensorwise(dev, n=16384):
-    log("generating %dx%d heavy-tailed bf16 input" % (n, n))
-    bits = workloads.heavy_tailed_rows(n, n, seed=2)
-    x = to_dev_bf16(bits, dev)
+    bits, x = square_input(dev, n)
     q = torch.empty((n, n), dtype=torch.uint8, device=dev)
     s = torch.empty(1, dtype=torch.int16, device=dev)
     ws = torch.empty(mx.mx_tensorwise_workspace_bytes(n * n), dtype=torch.uint8, device=dev)
@@ -951,6 +984,49 @@ WORKLOADS = {"square16384": setup_square, "square16384_3launch": setup_square_3l
              "cast_plain": lambda dev, **kw: setup_cast_shape(dev, plain=True, **kw)}
 
 
+# Further workloads measured by the default run (one entry each under
+# "configs"): the plain-scale call the headline's fused call replaces, the
+# MoE activation casts with grouped scales, the K-grouped layouts and the 3D
+# expert-weight cast.  They run before the headline's warm-up.
+EXTRAS = (
+    ("square16384_plain", setup_square_plain),
+    ("moe16640", setup_moe),
+    ("moe16640_both", setup_moe_both),
+    ("kgroups", setup_kgroups),
+    ("experts16", lambda dev: setup_experts(dev, device_inputs=True)),
+)
+
+
+def measure_extra(name, setup, dev, warmup=20, steps=100, cold=20):
+    """Back-to-back mean over `steps` launches (one event pair around them,
+    after `warmup`) and the cold-cache median over `cold` more, for one
+    workload; its buffers are released afterwards."""
+    step, step_bytes, timer, kern_bytes, kern_name, _, config = setup(dev)
+    scale = 1e12 if config.get("unit") == "TFLOP/s" else 1e9
+    unit = config.get("unit", "GB/s")
+    peak = config.get("peak", HBM_PEAK_GBS)
+    timer.reserve(warmup + steps)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    timer.clear()
+    timer.start_region()
+    for _ in range(steps):
+        step()
+    timer.end_region(steps)
+    torch.cuda.synchronize(dev)
+    us = timer.mean_ms() * 1e3
+    achieved = kern_bytes / (us * 1e-6) / scale
+    timer.reserve(cold)
+    c = cold_cache(step, step_bytes, cold, scale, unit, peak, dev)
+    log("%s: %.2f us, %.1f %s (%.1f%%); cold %.2f us" % (name, us, achieved, unit, 100 * achieved / peak,
+                                                         c["step_us_median"]))
+    return {"workload": config["workload"], "kernel": kern_name, "kernel_us": round(us, 2),
+            "achieved": round(achieved, 1), "unit": unit, "frac": round(achieved / peak, 4),
+            ("algorithmic_flops" if unit == "TFLOP/s" else "algorithmic_bytes"): kern_bytes,
+            "cold_us_median": c["step_us_median"], "cold_frac": c["frac"], "steps": steps, "warmup": warmup}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -962,6 +1038,8 @@ def main():
     ap.add_argument("--cols", type=int, default=None, help="cols of the cast_blocked / cast_grouped / cast_plain workloads")
     ap.add_argument("--cold-launches", type=int, default=50,
                     help="steps timed one by one after cache-evicting traffic (0: skip)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the further workloads the default run measures before the headline")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the cast and layout kernels run on one GPU's "
@@ -979,6 +1057,17 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     step, step_bytes, timer, kern_bytes, kern_name, cpu_fn, config = WORKLOADS[args.workload](dev, **shape)
+    extras = None
+    if args.workload == "square16384" and not args.no_extras:
+        # Measured first: they also bring the GPU out of its idle clocks (a
+        # process's first ~15-20 ms of launches, or the first after an idle
+        # second, run ~4% slower whatever they touch), so that a short
+        # warm-up of the headline reads its steady state.
+        extras = {}
+        for name, setup in EXTRAS:
+            extras[name] = measure_extra(name, setup, dev)
+            torch.cuda.synchronize(dev)
+            torch.cuda.empty_cache()
     timer.reserve(args.warmup + args.steps)
     torch.cuda.synchronize(dev)
     log("warmup %d steps" % args.warmup)
@@ -1008,11 +1097,18 @@ def main():
     achieved = kern_bytes / (kern_ms * 1e-3) / scale
     log("step %.2f us, %s %.2f us = %.1f %s" % (ms_per_step * 1e3, kern_name, kern_ms * 1e3, achieved, unit))
 
+    traffic = counter_traffic() if args.workload == "square16384" else None
     roofline = {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4),
-                "traffic": counter_traffic() if args.workload == "square16384" else None,
+                "traffic": traffic,
                 "kernel": kern_name, "kernel_us": round(kern_ms * 1e3, 2),
                 ("algorithmic_flops" if unit == "TFLOP/s" else "algorithmic_bytes"): kern_bytes}
+    if traffic is not None:
+        # not measured by this run: the committed counter summary's figure,
+        # used only while the kernel sources it was taken on are unchanged
+        roofline["traffic_source"] = ("rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE, stored in profiles/%s "
+                                      "(kernel sources digest %s)" % (os.path.basename(COUNTER_SUMMARY),
+                                                                       sources_digest()))
 
     cold = None
     if args.cold_launches > 0:
@@ -1029,6 +1125,8 @@ def main():
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
             "data": "synthetic", "config": config, "roofline": roofline, "cpu_baseline": cpu,
             "cold_cache": cold}
+    if extras is not None:
+        line["configs"] = extras
     print(json.dumps(line), flush=True)
 
 

@@ -35,5 +35,12 @@ def test_bench_json_line():
     assert roof["bound"] == "hbm" and roof["unit"] == "GB/s" and roof["peak"] == 8000.0
     assert roof["achieved"] > 0 and abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
     assert "traffic" in roof
+    if roof["traffic"] is not None:
+        assert "traffic_source" in roof
+    # the other workloads of the hot path, measured by the same run
+    assert set(d["configs"]) == {"square16384_plain", "moe16640", "moe16640_both", "kgroups", "experts16"}
+    for name, e in d["configs"].items():
+        assert e["kernel_us"] > 0 and 0 < e["frac"] < 1 and e["cold_us_median"] > 0, name
+        assert abs(e["achieved"] - e["algorithmic_bytes"] / (e["kernel_us"] * 1e3)) < 0.5, name
     cpu = d["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["cores"] >= 1 and cpu["value"] > 0 and cpu["matches_gpu"] is True
