@@ -8,18 +8,21 @@
 // bounded by rows + num_groups * 128; Perf analysis item 2: M-group, K-group
 // and per-expert 3D variants).
 //
-// One workgroup (256 threads) owns one 128-row block and up to 16
-// consecutive output tiles (16 column blocks of 4).  It stages the strip in
-// LDS with 64-byte contiguous reads per source row, then writes the 16
-// tiles: each store instruction of a wave writes two whole 512-byte tiles,
-// non-temporal (the lines are complete, so nothing is gained by keeping them
-// in the L2).  Workgroups are numbered so that each XCD (workgroups are
-// dispatched round-robin over the 8 XCDs) takes consecutive strips: the two
-// strips that read halves of the same source lines then share its L2.  The
-// source reads stay ordinary loads: each covers part of a line.  Chosen by
-// timing on MI355X against 8- and 32-tile strips, plain numbering, ordinary
-// stores and non-temporal loads (e.g. the (16, 5120, 256) per-expert layout:
-// 12.0 -> 6.6 us, K groups of (8192, 4096): 22.9 -> 18.7 us).  The
+// One workgroup (256 threads) owns one 128-row block and up to 16 or 32
+// consecutive output tiles (column blocks of 4; 32 where the grid still has
+// 512 workgroups).  It stages the strip in LDS with 64- or 128-byte
+// contiguous reads per source row, all of a thread's loads in flight at
+// once, then writes the tiles: each store instruction of a wave writes two
+// whole 512-byte tiles, non-temporal (the lines are complete, so nothing is
+// gained by keeping them in the L2).  Workgroups are numbered so that each
+// XCD (workgroups are dispatched round-robin over the 8 XCDs) takes
+// consecutive strips: strips that read parts of the same source lines then
+// share its L2.  The source reads stay ordinary loads: a 16-tile strip
+// covers half a line.  Chosen by timing on MI355X against 8-tile strips,
+// plain numbering, ordinary stores and non-temporal loads (e.g. the (16,
+// 5120, 256) per-expert layout: 12.0 -> 6.6 us, K groups of (8192, 4096):
+// 22.9 -> 18.7 us), then 32-tile strips and all loads in flight at once
+// (5.1 and 12.0 us).  The
 // grouped forms rebuild the group table (clamped ends, padded starts) in LDS
 // in every workgroup with one wave-wide scan, so the whole conversion is a
 // single launch with no host round trip.
@@ -36,11 +39,9 @@
 namespace mx {
 
 constexpr int kBlkThreads = 256;
-constexpr int kStripTiles = 16;
 constexpr int kXcdCount = 8;
 constexpr int kTileRows = 128;
 constexpr int kTileBytes = 512;
-constexpr int kLdsStride = kStripTiles + 1;  // dwords per staged row (+1 against bank conflicts)
 
 enum : int { kModeBatched = 0, kModeMGroups = 1, kModeKGroups = 2 };
 
@@ -60,13 +61,15 @@ struct Args {
   int64_t out_bytes;
   int64_t* out_starts;
   int64_t row_blocks;   // output row blocks in the grid
-  int64_t col_chunks;   // strips of kStripTiles tiles per row block in the grid
+  int64_t col_chunks;   // strips (of STRIP tiles) per row block in the grid
   int64_t blocks;       // workgroups doing work (the grid rounds up to 8 XCDs)
   int64_t per_xcd;      // consecutive work items per XCD
 };
 
-template <int MODE>
+template <int MODE, int STRIP>
 __global__ __launch_bounds__(kBlkThreads) void blocked_kernel(Args a) {
+  static_assert(STRIP % 8 == 0 && kBlkThreads % STRIP == 0, "a strip is whole store passes and load rows");
+  constexpr int kLdsStride = STRIP + 1;  // dwords per staged row (+1 against bank conflicts)
   __shared__ uint32_t strip[kTileRows * kLdsStride];
   __shared__ std::conditional_t<MODE == kModeBatched, NoTable, GroupTable> table;
 
@@ -119,7 +122,7 @@ __global__ __launch_bounds__(kBlkThreads) void blocked_kernel(Args a) {
 
   auto slot_of = [&](int k) -> Slot {
     Slot sl;
-    const int64_t cb = chunk * kStripTiles + k;
+    const int64_t cb = chunk * STRIP + k;
     if constexpr (MODE == kModeKGroups) {
       const int64_t tcb = ncb + a.groups;
       if (cb >= tcb) {
@@ -155,25 +158,38 @@ __global__ __launch_bounds__(kBlkThreads) void blocked_kernel(Args a) {
   };
 
   // Stage: row i, tile k -> one dword (4 scale bytes, column order = byte order).
+  // A thread keeps one tile k and takes every (256 / STRIP)-th row; when its
+  // tile's 4 source columns are a whole aligned dword, all of its loads are
+  // issued at once as buffer loads ranged to the block's valid rows (rows
+  // past them read zero), else it assembles the bytes one by one.
   {
-    const int k = tid % kStripTiles;
+    constexpr int kRowsPerPass = kBlkThreads / STRIP;
+    constexpr int kPasses = kTileRows / kRowsPerPass;
+    const int k = tid % STRIP;
+    const int i0 = tid / STRIP;
     const Slot sl = slot_of(k);
     const bool aligned = sl.ncols == 4 && (a.cols % 4) == 0 && (sl.src_col % 4) == 0 &&
-                         ((uintptr_t)src % 4) == 0;
+                         ((uintptr_t)src % 4) == 0 && a.cols < (1 << 23);
+    if (aligned && nrows > 0) {
+      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(src + row0 * a.cols, (uint32_t)(nrows * a.cols));
+      uint32_t v[kPasses];
 #pragma unroll
-    for (int p = 0; p < kTileRows / (kBlkThreads / kStripTiles); ++p) {
-      const int i = p * (kBlkThreads / kStripTiles) + tid / kStripTiles;
-      uint32_t v = 0;
-      if (i < nrows && sl.ncols > 0) {
-        const uint8_t* sp = src + (row0 + i) * a.cols + sl.src_col;
-        if (aligned) {
-          v = *reinterpret_cast<const uint32_t*>(sp);
-        } else {
+      for (int p = 0; p < kPasses; ++p)
+        v[p] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)((i0 + p * kRowsPerPass) * a.cols + sl.src_col), 0, 0);
+#pragma unroll
+      for (int p = 0; p < kPasses; ++p)
+        strip[(i0 + p * kRowsPerPass) * kLdsStride + k] = v[p];
+    } else {
+      for (int p = 0; p < kPasses; ++p) {
+        const int i = i0 + p * kRowsPerPass;
+        uint32_t v = 0;
+        if (i < nrows && sl.ncols > 0) {
+          const uint8_t* sp = src + (row0 + i) * a.cols + sl.src_col;
           for (int j = 0; j < sl.ncols; ++j)
             v |= (uint32_t)sp[j] << (8 * j);
         }
+        strip[i * kLdsStride + k] = v;
       }
-      strip[i * kLdsStride + k] = v;
     }
   }
   __syncthreads();
@@ -186,7 +202,7 @@ __global__ __launch_bounds__(kBlkThreads) void blocked_kernel(Args a) {
     const int wave = tid >> 6;
     const int i = tid & 31;
 #pragma unroll
-    for (int h = 0; h < kStripTiles / 8; ++h) {
+    for (int h = 0; h < STRIP / 8; ++h) {
       const int k = 8 * h + 2 * wave + ((tid >> 5) & 1);
       const Slot sl = slot_of(k);
       if (sl.out_off >= 0) {
@@ -205,28 +221,41 @@ __global__ __launch_bounds__(kBlkThreads) void blocked_kernel(Args a) {
   }
 }
 
-// Work items of a launch (row blocks x strips), 0 when there is nothing to do.
-static int64_t plan_blocked(int mode, Args& a) {
+// Work items of a launch (row blocks x strips of `strip` tiles), 0 when
+// there is nothing to do.
+static int64_t plan_blocked(int mode, Args& a, int strip) {
   const int64_t ncb = (a.cols + 3) / 4;
   const int64_t rb = (a.rows + kTileRows - 1) / kTileRows;
   if (mode == kModeBatched) {
     a.row_blocks = rb;
-    a.col_chunks = (ncb + kStripTiles - 1) / kStripTiles;
+    a.col_chunks = (ncb + strip - 1) / strip;
     return a.batch * a.row_blocks * a.col_chunks;
   }
   // Grouped forms always launch at least one workgroup: the padded starts
   // are written even when the scale matrix is empty.
   if (mode == kModeMGroups) {
     a.row_blocks = (a.rows + (int64_t)kTileRows * a.groups + kTileRows - 1) / kTileRows;
-    a.col_chunks = (ncb + kStripTiles - 1) / kStripTiles;
+    a.col_chunks = (ncb + strip - 1) / strip;
   } else {
     a.row_blocks = rb;
-    a.col_chunks = (ncb + a.groups + kStripTiles - 1) / kStripTiles;
+    a.col_chunks = (ncb + a.groups + strip - 1) / strip;
   }
   a.row_blocks = a.row_blocks > 0 ? a.row_blocks : 1;
   a.col_chunks = a.col_chunks > 0 ? a.col_chunks : 1;
   a.batch = 1;
   return a.row_blocks * a.col_chunks;
+}
+
+// Strip width: 32 tiles (128 source bytes per row) where that still gives
+// the launch kBlkWideMin workgroups, else 16.  Timed on MI355X (back to back,
+// 300 launches): K groups of (8192, 4096) 13.3 us with 16-tile strips, 12.0
+// with 32, 13.9 with 64; the (16, 5120, 256) per-expert layout 5.2 / 5.1 /
+// 5.4 us; the small grids (M groups of (16640, 160): 268 workgroups of 32
+// tiles) 4.1 us with 16 against 4.9 with 32.
+constexpr int64_t kBlkWideMin = 512;
+static int strip_of(int mode, const Args& a0) {
+  Args a = a0;
+  return plan_blocked(mode, a, 32) >= kBlkWideMin ? 32 : 16;
 }
 
 int64_t blocked_grid_blocks(int32_t mode, int64_t batch, int64_t rows, int64_t cols, int32_t groups) {
@@ -235,23 +264,33 @@ int64_t blocked_grid_blocks(int32_t mode, int64_t batch, int64_t rows, int64_t c
   a.rows = rows;
   a.cols = cols;
   a.groups = groups;
-  const int64_t items = plan_blocked(mode, a);
+  // the narrowest strip gives the largest grid
+  const int64_t items = plan_blocked(mode, a, 16);
   return (items + kXcdCount - 1) / kXcdCount * kXcdCount;
+}
+
+template <int MODE>
+static void launch_mode(const Args& a, int strip, dim3 grid, hipStream_t stream) {
+  if (strip == 32)
+    hipLaunchKernelGGL((blocked_kernel<MODE, 32>), grid, dim3(kBlkThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((blocked_kernel<MODE, 16>), grid, dim3(kBlkThreads), 0, stream, a);
 }
 
 static hipError_t launch_blocked(int mode, const Args& a0, hipStream_t stream) {
   Args a = a0;
-  a.blocks = plan_blocked(mode, a);
+  const int strip = strip_of(mode, a0);
+  a.blocks = plan_blocked(mode, a, strip);
   if (a.blocks == 0)
     return hipSuccess;
   a.per_xcd = (a.blocks + kXcdCount - 1) / kXcdCount;
   const dim3 grid((unsigned)(a.per_xcd * kXcdCount));
   if (mode == kModeBatched)
-    hipLaunchKernelGGL(blocked_kernel<kModeBatched>, grid, dim3(kBlkThreads), 0, stream, a);
+    launch_mode<kModeBatched>(a, strip, grid, stream);
   else if (mode == kModeMGroups)
-    hipLaunchKernelGGL(blocked_kernel<kModeMGroups>, grid, dim3(kBlkThreads), 0, stream, a);
+    launch_mode<kModeMGroups>(a, strip, grid, stream);
   else
-    hipLaunchKernelGGL(blocked_kernel<kModeKGroups>, grid, dim3(kBlkThreads), 0, stream, a);
+    launch_mode<kModeKGroups>(a, strip, grid, stream);
   return hipGetLastError();
 }
 
