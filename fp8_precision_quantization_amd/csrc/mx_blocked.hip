@@ -327,7 +327,9 @@ hipError_t launch_blocked_grouped(const uint8_t* s, int64_t rows, int64_t cols, 
 // plain row-major one.  A 128-row band occupies the same 128 * C bytes in
 // both layouts (in the blocked one as its C / 4 tiles, one after another), so
 // one workgroup per band reads the whole band with contiguous 16-byte loads,
-// regroups it in LDS and writes it back as contiguous rows.  Dword j of chunk
+// regroups it in LDS and writes it back as contiguous rows, in 16-byte
+// chunks when a row is whole chunks (1.2 us less than dword stores at 16384
+// x 16384, where both 16384 x 512 matrices go through it).  Dword j of chunk
 // i of tile k is row i + 32 j, scale columns 4 k .. 4 k + 3.  Every load of a
 // band has returned (its value is in LDS) before the barrier, and only after
 // it does any thread of the workgroup store into the band.
@@ -371,8 +373,33 @@ __global__ __launch_bounds__(kUnblockThreads) void unblock_kernel(uint8_t* m0, i
     }
   }
   __syncthreads();
-  // plain dword d = r * tiles + k for d = t, t + 1024, ...; all LDS reads
-  // first, then the stores
+  // Rows of whole 16-byte chunks (tiles % 4 == 0): plain chunk e = r *
+  // (tiles / 4) + j (dwords 4 j .. 4 j + 3 of row r) for e = t, t + 1024,
+  // ...; else plain dword d = r * tiles + k for d = t, t + 1024, ...  All LDS
+  // reads first, then the stores.
+  if (tiles % 4 == 0) {
+    uint4* out = reinterpret_cast<uint4*>(base);
+    const int per_row = tiles / 4;
+    const int total = per_row * kTileRows;
+    constexpr int kChunks = kUnblockDwords / 4;
+    uint4 w[kChunks];
+#pragma unroll
+    for (int n = 0; n < kChunks; ++n) {
+      const int e = t + kUnblockThreads * n;
+      if (e < total) {
+        const int r = e / per_row, j = e - r * per_row;
+        const uint32_t* src = &staged[r * kUnblockPitch + 4 * j];
+        w[n] = make_uint4(src[0], src[1], src[2], src[3]);
+      }
+    }
+#pragma unroll
+    for (int n = 0; n < kChunks; ++n) {
+      const int e = t + kUnblockThreads * n;
+      if (e < total)
+        out[e] = w[n];
+    }
+    return;
+  }
   uint32_t* out = reinterpret_cast<uint32_t*>(base);
   const int total = tiles * kTileRows;
   const int step_r = kUnblockThreads / tiles, step_k = kUnblockThreads % tiles;

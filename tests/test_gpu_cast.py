@@ -76,8 +76,11 @@ def test_single_direction(oracle_mod, dim0, dim1):
 # layout and converted back to rows in place, one 128-row band per workgroup
 # (16384 x 16384 is covered by the full-size configuration test).  16512 rows
 # take that path for dim0 alone (their dim1 scale rows are too long);
-# 3968 columns sit just under the size bound (direct path).
-VIA_BLOCKED = [(16384, 4096), (16512, 4096), (16384, 3968)]
+# 3968 columns sit just under the size bound (direct path); 4224 columns
+# give 33 blocked tiles per 128-row band of the row scales, which the
+# in-place conversion writes back as dwords (whole 16-byte chunks need a
+# multiple of 4 tiles).
+VIA_BLOCKED = [(16384, 4096), (16512, 4096), (16384, 3968), (16384, 4224)]
 
 
 @pytest.mark.parametrize("dim0,dim1", [(True, True), (True, False), (False, True)])
