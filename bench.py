@@ -219,22 +219,31 @@ class Timer:
         return sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
 
 
-def c_call(name, *args):
+def c_call(name, *args, stream_at_call=False):
     """A C-ABI entry point with its arguments marshalled once (tensors become
     device pointers, plus torch's current stream), for the timed loops; the
     Python binding of the same name validates the same call during set-up.
-    The returned call keeps its tensors alive: a tensor known to it only by
-    its address would go back to torch's allocator once the set-up returns,
-    and the next allocation (the cold-cache buffers, say) could take it over."""
+    stream_at_call: look torch's current stream up at each call instead (so
+    that the call can be captured into a graph, whose capture runs on a
+    stream of its own).  The returned call keeps its tensors alive: a tensor
+    known to it only by its address would go back to torch's allocator once
+    the set-up returns, and the next allocation (the cold-cache buffers, say)
+    could take it over."""
     f = getattr(mx.lib(), name)
     conv = [ctypes.c_void_p(a.data_ptr()) if isinstance(a, torch.Tensor) else a for a in args]
-    conv.append(ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
     keep = [a for a in args if isinstance(a, torch.Tensor)]
+    if stream_at_call:
+        def call():
+            rc = f(*conv, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+            if rc != 0:
+                raise mx.MxError(rc, name)
+    else:
+        conv.append(ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
 
-    def call():
-        rc = f(*conv)
-        if rc != 0:
-            raise mx.MxError(rc, name)
+        def call():
+            rc = f(*conv)
+            if rc != 0:
+                raise mx.MxError(rc, name)
     call.tensors = keep
     return call
 
@@ -569,7 +578,7 @@ def setup_kgroups(dev):
     for s, offs, out, starts in items:
         mx.mx_scales_to_blocked_grouped(s, offs, 1, out=out, out_group_starts=starts, raw=True)
         calls.append(c_call("mx_scales_to_blocked_grouped", s, s.shape[0], s.shape[1], offs, offs.numel(), 1,
-                            out, starts))
+                            out, starts, stream_at_call=True))
 
     def step():
         with timer:
@@ -593,6 +602,9 @@ def setup_kgroups(dev):
 
     config = {"workload": "K-grouped blocked layout of e8m0 scales %s, 4 groups each"
                           % (list(workloads.K_GROUP_SHAPES),),
+              # the three launches last ~20 us together, less than the host
+              # takes to issue them: measured as replays of a captured graph
+              "graph_steps": 20,
               "metric": "achieved HBM GB/s (% of MI355X peak) for the K-grouped 128x4 blocked layout of e8m0 "
                         "scales",
               "dtype": "u8"}
@@ -997,25 +1009,55 @@ EXTRAS = (
 )
 
 
+def graph_step_us(step, graph_steps, steps, dev):
+    """Mean time of a step replayed from a captured graph of `graph_steps`
+    steps (one event pair around steps // graph_steps replays): the GPU runs
+    the launches back to back, whatever the host's time to issue them."""
+    torch.cuda.synchronize(dev)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(graph_steps):
+            step()
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize(dev)
+    reps = max(1, steps // graph_steps)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize(dev)
+    us = e0.elapsed_time(e1) * 1e3 / (reps * graph_steps)
+    del g
+    return us, reps * graph_steps
+
+
 def measure_extra(name, setup, dev, warmup=20, steps=100, cold=20):
     """Back-to-back mean over `steps` launches (one event pair around them,
-    after `warmup`) and the cold-cache median over `cold` more, for one
-    workload; its buffers are released afterwards."""
+    after `warmup`; replays of a captured graph for workloads whose launches
+    are shorter than the host's time to issue them) and the cold-cache
+    median over `cold` more, for one workload; its buffers are released
+    afterwards."""
     step, step_bytes, timer, kern_bytes, kern_name, _, config = setup(dev)
     scale = 1e12 if config.get("unit") == "TFLOP/s" else 1e9
     unit = config.get("unit", "GB/s")
     peak = config.get("peak", HBM_PEAK_GBS)
+    graph_steps = config.get("graph_steps", 0)
     timer.reserve(warmup + steps)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize(dev)
     timer.clear()
-    timer.start_region()
-    for _ in range(steps):
-        step()
-    timer.end_region(steps)
-    torch.cuda.synchronize(dev)
-    us = timer.mean_ms() * 1e3
+    if graph_steps:
+        us, steps = graph_step_us(step, graph_steps, steps, dev)
+    else:
+        timer.start_region()
+        for _ in range(steps):
+            step()
+        timer.end_region(steps)
+        torch.cuda.synchronize(dev)
+        us = timer.mean_ms() * 1e3
     achieved = kern_bytes / (us * 1e-6) / scale
     timer.reserve(cold)
     c = cold_cache(step, step_bytes, cold, scale, unit, peak, dev)
@@ -1024,7 +1066,8 @@ def measure_extra(name, setup, dev, warmup=20, steps=100, cold=20):
     return {"workload": config["workload"], "kernel": kern_name, "kernel_us": round(us, 2),
             "achieved": round(achieved, 1), "unit": unit, "frac": round(achieved / peak, 4),
             ("algorithmic_flops" if unit == "TFLOP/s" else "algorithmic_bytes"): kern_bytes,
-            "cold_us_median": c["step_us_median"], "cold_frac": c["frac"], "steps": steps, "warmup": warmup}
+            "cold_us_median": c["step_us_median"], "cold_frac": c["frac"], "steps": steps, "warmup": warmup,
+            **({"graph_steps": graph_steps} if graph_steps else {})}
 
 
 def main():
@@ -1091,6 +1134,7 @@ def main():
     metric = config.pop("metric", METRIC)
     dtype = config.pop("dtype", "bf16")
     bound = config.pop("bound", "hbm")
+    config.pop("graph_steps", None)
     peak = config.pop("peak", HBM_PEAK_GBS)
     value = step_bytes / (ms_per_step * 1e-3) / scale
     kern_ms = timer.mean_ms()
