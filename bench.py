@@ -46,8 +46,9 @@ The default run also measures, before the headline's warm-up, the other
 workloads of the hot path (the `configs` object: the plain-scale call
 mx_cast_dim0_dim1 at 16384 x 16384, the MoE casts with M-grouped and with
 both scale sets grouped, the three K-grouped layouts and the 3D expert cast;
-each its back-to-back mean over 100 launches and its cold-cache median over
-20; --no-extras skips them).
+each its back-to-back mean over 100 launches, after at least 20 steps and
+25 ms of warm-up, and its cold-cache median over 20; --no-extras skips
+them).
 
 Prints exactly one JSON line on stdout; progress goes to stderr.  The
 `roofline` object is for the dominant kernel (the cast): algorithmic bytes per
@@ -1044,10 +1045,17 @@ def measure_extra(name, setup, dev, warmup=20, steps=100, cold=20):
     unit = config.get("unit", "GB/s")
     peak = config.get("peak", HBM_PEAK_GBS)
     graph_steps = config.get("graph_steps", 0)
+    # warm-up: at least `warmup` steps and 25 ms of them, so that a workload
+    # measured first still runs at the GPU's steady clocks
     timer.reserve(warmup + steps)
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    done = 0
+    while done < warmup or time.perf_counter() - t0 < 0.025:
+        for _ in range(10):
+            step()
+        done += 10
+        torch.cuda.synchronize(dev)
+        timer.clear()
     timer.clear()
     if graph_steps:
         us, steps = graph_step_us(step, graph_steps, steps, dev)
@@ -1066,7 +1074,7 @@ def measure_extra(name, setup, dev, warmup=20, steps=100, cold=20):
     return {"workload": config["workload"], "kernel": kern_name, "kernel_us": round(us, 2),
             "achieved": round(achieved, 1), "unit": unit, "frac": round(achieved / peak, 4),
             ("algorithmic_flops" if unit == "TFLOP/s" else "algorithmic_bytes"): kern_bytes,
-            "cold_us_median": c["step_us_median"], "cold_frac": c["frac"], "steps": steps, "warmup": warmup,
+            "cold_us_median": c["step_us_median"], "cold_frac": c["frac"], "steps": steps, "warmup": done,
             **({"graph_steps": graph_steps} if graph_steps else {})}
 
 
