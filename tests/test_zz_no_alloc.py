@@ -82,3 +82,35 @@ def test_noalloc_binding_and_empty_input(oracle_mod):
     assert_bytes_equal(host(q), r_q, "binding q")
     q0, _ = mx.mx_quantize_fp8_tensorwise_noalloc(torch.empty(0, dtype=torch.bfloat16, device=dev), raw=True)
     assert q0.numel() == 0
+
+
+def test_noalloc_under_graph_capture(oracle_mod):
+    """The allocation-free cast captured into a graph (with its outputs
+    preallocated, nothing in the captured work allocates) and replayed three
+    times, with eager work and a synchronisation between replays: every
+    replay gives the eager call's bytes."""
+    dev = device()
+    bits = _spread(3_000_001, seed=4, log2_scale=5)
+    x = to_dev_bf16(bits, dev)
+    q_e, s_e = _outs(bits.size, dev, 0xCD)
+    mx.mx_quantize_fp8_tensorwise_noalloc(x, out=(q_e, s_e), raw=True)
+    torch.cuda.synchronize(dev)
+    q_g, s_g = _outs(bits.size, dev, 0x33)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        mx.mx_quantize_fp8_tensorwise_noalloc(x, out=(q_g, s_g), raw=True)
+    other = _spread(50_000, seed=5, log2_scale=9)
+    y = to_dev_bf16(other, dev)
+    for rep in range(3):
+        q_g.fill_(0x33)
+        s_g.fill_(0x5A5A)
+        g.replay()
+        torch.cuda.synchronize(dev)
+        assert _scale_bits(s_g) == _scale_bits(s_e), rep
+        assert_bytes_equal(host(q_g), host(q_e), "replay %d q" % rep)
+        # eager work on the same scratch between replays
+        mx.mx_quantize_fp8_tensorwise_noalloc(y, raw=True)
+        torch.cuda.synchronize(dev)
+    r_q, r_s = oracle_mod.quantize_fp8_tensorwise(bits)
+    assert _scale_bits(s_e) == r_s
+    assert_bytes_equal(host(q_e), r_q, "eager q vs oracle")
