@@ -733,10 +733,20 @@ int64_t cast_grid_blocks(int64_t rows, int64_t cols) {
   return blocks;
 }
 
+// The dim1-only casts (3D expert weights) run faster with 2 workgroups per
+// CU than with the 4 their registers allow: each launch reserves this much
+// LDS beyond what the kernel uses, so that only two fit a CU's 160 KiB.
+// Timed on MI355X at (16, 8192, 5120), A/B/A/B: with blocked scales 345.8
+// -> 340.9 us, with plain scales 359.7 -> 345.1 us (3 per CU: 344.6 and
+// 356.3 us).  The dim0+dim1 casts are slower with fewer than 3 (16384^2:
+// 160.9 -> 164.2 us at 2 per CU).
+constexpr size_t kDim1OnlyExtraLds = 20 * 1024;
+
 template <bool DIM0, bool DIM1, bool BLK, bool MGRP = false, bool KGRP = false>
 static hipError_t launch_cast(const CastArgs& a, int64_t blocks, hipStream_t stream) {
-  hipLaunchKernelGGL((cast_kernel<DIM0, DIM1, BLK, MGRP, KGRP>), dim3((unsigned)blocks), dim3(kWaves * 64), 0,
-                     stream, a);
+  const size_t extra_lds = (!DIM0 && DIM1) ? kDim1OnlyExtraLds : 0;
+  hipLaunchKernelGGL((cast_kernel<DIM0, DIM1, BLK, MGRP, KGRP>), dim3((unsigned)blocks), dim3(kWaves * 64),
+                     extra_lds, stream, a);
   return hipGetLastError();
 }
 
