@@ -80,11 +80,14 @@ mx_status mx_cast_dim0_dim1(const void* x, int64_t rows, int64_t cols, uint8_t* 
   // LDS, the scales are written in the blocked layout, whose stores are whole
   // lines, and then turned into the plain one in place (the same bytes).
   // Timed on MI355X against the direct kernel's partial 1- and 4-byte scale
-  // runs: 16384 x 16384 174 against 181 us, 16384 x 4096 55 against 61 us,
-  // 16384 x 8192 and 8192 x 16384 about even; 4096 x 16384 and every smaller
-  // input slower (the conversion's own ~5-11 us and second launch), hence
-  // the size bound.
-  const bool via_blocked = rows >= 16384 && cols >= 4096 && rows % 128 == 0 && cols % 128 == 0 &&
+  // runs (both directions, 150 calls after 40): 16384 x 16384 170 against
+  // 181 us, 16384 x 4096 52 against 61, 16384 x 8192 and 8192 x 16384 91
+  // against 92, 32768 x 8192 174 against 187, 32768 x 16384 421 against 438;
+  // slower at 16640 x 5120 (68 against 61), 32768 x 4096 (98 against 92),
+  // 4096 x 16384, 8192 x 8192 and every smaller input (the conversion's own
+  // ~5-8 us and second launch), hence the bounds.
+  const bool big = (rows >= 16384 && cols >= 8192) || (rows == 16384 && cols >= 4096);
+  const bool via_blocked = big && rows % 128 == 0 && cols % 128 == 0 &&
                            (!d0 || (cols / MX_BLOCK <= mx::kUnblockMaxCols && aligned(s_row, 16))) &&
                            (!d1 || (rows / MX_BLOCK <= mx::kUnblockMaxCols && aligned(s_col, 16)));
   if (via_blocked) {

@@ -329,7 +329,13 @@ hipError_t launch_blocked_grouped(const uint8_t* s, int64_t rows, int64_t cols, 
 // one workgroup per band reads the whole band with contiguous 16-byte loads,
 // regroups it in LDS and writes it back as contiguous rows, in 16-byte
 // chunks when a row is whole chunks (1.2 us less than dword stores at 16384
-// x 16384, where both 16384 x 512 matrices go through it).  Dword j of chunk
+// x 16384, where both 16384 x 512 matrices go through it).  The band loads
+// are non-temporal: the cast has just written the band with non-temporal
+// stores, and cached loads of it took ~4 us longer at 16384 x 16384 (172 ->
+// 168 us for the whole plain-scale call), although a kernel that reads the
+// plain scales right after then takes longer (the two layout launches of
+// both 16384 x 512 matrices ~5 us more); the whole-line 16-byte stores are
+// non-temporal too (0.2 us).  Dword j of chunk
 // i of tile k is row i + 32 j, scale columns 4 k .. 4 k + 3.  Every load of a
 // band has returned (its value is in LDS) before the barrier, and only after
 // it does any thread of the workgroup store into the band.
@@ -359,7 +365,10 @@ __global__ __launch_bounds__(kUnblockThreads) void unblock_kernel(uint8_t* m0, i
   for (int n = 0; n < kUnblockChunks; ++n) {
     const int q = t + kUnblockThreads * n;
     if (q < chunks)
-      v[n] = *reinterpret_cast<const uint4*>(base + 16 * (int64_t)q);
+      {
+        const u32x4 l = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + 16 * (int64_t)q));
+        v[n] = make_uint4(l[0], l[1], l[2], l[3]);
+      }
   }
 #pragma unroll
   for (int n = 0; n < kUnblockChunks; ++n) {
@@ -396,7 +405,7 @@ __global__ __launch_bounds__(kUnblockThreads) void unblock_kernel(uint8_t* m0, i
     for (int n = 0; n < kChunks; ++n) {
       const int e = t + kUnblockThreads * n;
       if (e < total)
-        out[e] = w[n];
+        store_line_nt(reinterpret_cast<uint8_t*>(out + e), w[n]);
     }
     return;
   }

@@ -35,8 +35,9 @@ hipError_t launch_blocked_grouped(const uint8_t* s, int64_t rows, int64_t cols, 
 
 // In place, blocked -> plain: scale matrices m0 (r0 x c0 bytes) and m1 (r1 x
 // c1), either may be null; rows multiples of 128, columns multiples of 4 and
-// at most kUnblockMaxCols, 16-byte aligned.
-constexpr int64_t kUnblockMaxCols = 512;
+// at most kUnblockMaxCols (a 128-row band then fills 128 KiB of LDS), 16-byte
+// aligned.
+constexpr int64_t kUnblockMaxCols = 1024;
 hipError_t launch_unblock_inplace(uint8_t* m0, int64_t r0, int64_t c0, uint8_t* m1, int64_t r1, int64_t c1,
                                   hipStream_t stream);
 

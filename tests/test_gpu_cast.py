@@ -71,16 +71,17 @@ def test_single_direction(oracle_mod, dim0, dim1):
     check_cast(oracle_mod, bits, dev, "single", dim0=dim0, dim1=dim1)
 
 
-# At least 16384 rows and 4096 cols, multiples of 128, at most 512 scale
-# columns in each scale matrix present: the scales are written in the blocked
-# layout and converted back to rows in place, one 128-row band per workgroup
-# (16384 x 16384 is covered by the full-size configuration test).  16512 rows
-# take that path for dim0 alone (their dim1 scale rows are too long);
-# 3968 columns sit just under the size bound (direct path); 4224 columns
+# At least 16384 rows and 8192 cols (or exactly 16384 rows and at least
+# 4096 cols), multiples of 128, at most 1024 scale columns in each scale
+# matrix present: the scales are written in the blocked layout and converted
+# back to rows in place, one 128-row band per workgroup (16384 x 16384 is
+# covered by the full-size configuration test).  16512 x 4096 is under the
+# size bound (direct path), as are 3968 columns at 16384 rows; 4224 columns
 # give 33 blocked tiles per 128-row band of the row scales, which the
 # in-place conversion writes back as dwords (whole 16-byte chunks need a
-# multiple of 4 tiles).
-VIA_BLOCKED = [(16384, 4096), (16512, 4096), (16384, 3968), (16384, 4224)]
+# multiple of 4 tiles); 16640 x 8192 has 520-column dim1 scales (130 tiles
+# per band, past 512 columns, written back as dwords).
+VIA_BLOCKED = [(16384, 4096), (16512, 4096), (16384, 3968), (16384, 4224), (16640, 8192)]
 
 
 @pytest.mark.parametrize("dim0,dim1", [(True, True), (True, False), (False, True)])
@@ -89,6 +90,15 @@ def test_scales_through_blocked_layout(oracle_mod, shape, dim0, dim1):
     dev = device()
     bits = workloads.special_values_bf16(shape, seed=[23, shape[0], shape[1]], p_special=0.001)
     check_cast(oracle_mod, bits, dev, "%s dim0=%s dim1=%s" % (shape, dim0, dim1), dim0=dim0, dim1=dim1)
+
+
+def test_scales_through_blocked_layout_widest(oracle_mod):
+    """32768 x 8192: dim1 scale rows of 1024 bytes, the widest band the
+    in-place conversion takes (256 tiles, its whole LDS)."""
+    dev = device()
+    shape = (32768, 8192)
+    bits = workloads.special_values_bf16(shape, seed=[31, shape[0], shape[1]], p_special=0.0005)
+    check_cast(oracle_mod, bits, dev, "%s widest band" % (shape,))
 
 
 def test_scales_off_16_byte_alignment(oracle_mod):
