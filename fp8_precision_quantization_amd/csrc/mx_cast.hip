@@ -24,12 +24,20 @@
 // the same way and leave as one 4-byte run per column.  The barrier between
 // the two orders LDS only: __syncthreads() would also wait for global memory.
 //
-// Cache policy of the stores, by timing on MI355X (16384 x 16384, blocked
-// scales: 215 -> 163 us, outputs unchanged): the stores that write whole
-// 128-byte lines -- the staged dim1 codes and the blocked scale chunks -- are
-// non-temporal; the dim0 row segments and the plain scale runs, whose lines
-// are completed by neighbouring lanes and workgroups in the L2, stay
-// ordinary (non-temporal there cost time).
+// Cache policy of the stores, by timing on MI355X (outputs unchanged):
+// - the stores that write whole 128-byte lines -- the staged dim1 codes and
+//   the blocked scale chunks -- are non-temporal while the col-major output
+//   is larger than 128 MiB (16384 x 16384, blocked scales: 215 -> 163 us
+//   against ordinary stores), and written through to memory (sc0 sc1) up to
+//   that size, where that is faster again (16640 x 5120 M-grouped: 63.1 ->
+//   60.8 us; at 16384 x 16384 it would be 160.6 -> 201 us): 30 shapes from
+//   4096 x 2048 to 32768 x 16384 split cleanly at that size, which is where
+//   the two code matrices stop fitting the 256 MB memory-side cache;
+// - the dim0 row segments, whose lines neighbouring lanes complete, are
+//   written through (sc0 sc1: 16384 x 16384 161.0 -> 160.6 us, 16640 x 5120
+//   63.5 -> 63.1 us; non-temporal there cost time);
+// - the plain scale runs, whose lines neighbouring workgroups complete in
+//   the L2, stay ordinary (written through they cost 1 us at 16640 x 5120).
 //
 // With BLK the scales come out directly in the 128x4 blocked layout that
 // grouped GEMMs read ("[mxfp8 moe training] parallelize along col blocks in
@@ -66,9 +74,19 @@ constexpr int kTileCols = 32 * kLaneCols;       // 256
 constexpr int kXcds = 8;
 constexpr int kSlots = kTileRows / 16;          // 16-byte slots per staged column (8)
 constexpr int kLoadNT = 2;                      // cache-policy bits of the input loads: nt
+constexpr int kStoreWT = 17;                    // ... of stores written through: sc0 sc1
+constexpr int64_t kWriteThroughMax = 128 << 20; // largest col-major output whose lines are written through
 constexpr uint32_t kRowGroupBlocked = 2;        // see cast_args
 constexpr uint32_t kRowGroupPlain = 8;
 constexpr uint32_t kRowGroupDim1 = 1024;
+
+// 16 bytes that, across the lanes of one instruction, make up whole 128-byte
+// lines, written through, at byte offset off of buffer rs.  (The
+// non-temporal form is store_line_nt: as a buffer store it was ~1% slower at
+// 16384 x 16384 and (16, 8192, 5120).)
+__device__ __forceinline__ void store_line_wt(__amdgpu_buffer_rsrc_t rs, uint32_t off, const uint4& v) {
+  __builtin_amdgcn_raw_buffer_store_b128((u32x4){v.x, v.y, v.z, v.w}, rs, off, 0, kStoreWT);
+}
 
 __device__ __forceinline__ uint32_t word(const uint4& v, int k) {
   return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
@@ -142,8 +160,8 @@ __device__ __forceinline__ void dim0_rows(const uint4 (&d)[kLaneRows], const uin
       ba = __float_as_uint(p.scale_a) >> 23;
       bb = __float_as_uint(p.scale_b) >> 23;
     }
-    __builtin_amdgcn_raw_buffer_store_b64((u32x2){qa0, qa1}, q0, q0_off, (int)(i * cols), 0);
-    __builtin_amdgcn_raw_buffer_store_b64((u32x2){qb0, qb1}, q0, q0_off, (int)((i + 1) * cols), 0);
+    __builtin_amdgcn_raw_buffer_store_b64((u32x2){qa0, qa1}, q0, q0_off, (int)(i * cols), kStoreWT);
+    __builtin_amdgcn_raw_buffer_store_b64((u32x2){qb0, qb1}, q0, q0_off, (int)((i + 1) * cols), kStoreWT);
     if (quad_leader) {
       if (IMG != 0) {
         // rows i, i+1 of the lane are consecutive rows of the tile
@@ -220,6 +238,7 @@ struct CastArgs {
   uint32_t row_tiles, col_tiles, per_xcd;
   uint32_t row_group;  // row bands that run side by side on one XCD
   uint32_t rotate;     // XCD pieces start at points of their own (tile_of)
+  uint32_t wt;         // whole-line stores written through, else non-temporal
   // Blocked scale outputs: column blocks of the dim0 scale matrix, of one
   // segment's dim1 scale matrix, and that matrix's size in bytes.
   int64_t ncb0, ncb1, seg_blk_bytes;
@@ -600,7 +619,13 @@ __global__ __launch_bounds__(256) void cast_kernel(CastArgs a) {
       if (cb < a.ncb0) {
         uint4 v = reinterpret_cast<const uint4*>(s0_blk)[t * 32 + i];
         v = mask_chunk(v, valid_rows / 32, (int)min((int64_t)4, cols / 32 - 4 * cb));
-        store_line_nt(a.s0 + ((int64_t)rt * a.ncb0 + cb) * 512 + i * 16, v);
+        if (a.wt != 0) {
+          // The workgroup's two blocked tiles are 1024 consecutive bytes.
+          const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(a.s0 + ((int64_t)rt * a.ncb0 + 2 * (int64_t)ct) * 512, 1024);
+          store_line_wt(rs, lane * 16, v);
+        } else {
+          store_line_nt(a.s0 + ((int64_t)rt * a.ncb0 + cb) * 512 + i * 16, v);
+        }
       }
     }
   }
@@ -617,19 +642,36 @@ __global__ __launch_bounds__(256) void cast_kernel(CastArgs a) {
     const int64_t seg_blocks = rps / 32;
     // Codes: 8 lanes per column, 16 bytes each; a wave covers 8 columns per pass.
     const int slot = threadIdx.x & 7;
+    // Written through: within one segment the tile's columns are output rows
+    // tc .. tc + 255 of that segment, rps bytes apart, which one buffer
+    // covers while they span less than 2 GiB (else non-temporal).  The loop
+    // is written once per policy, the choice taken outside it.
+    const bool wt = a.wt != 0 && one_seg && (int64_t)kTileCols * rps < (1ll << 31);
+    const auto put_codes = [&](auto wt_tag) {
+      constexpr bool WT = decltype(wt_tag)::value;
+      const __amdgpu_buffer_rsrc_t q1rs = buffer_rsrc(a.q1 + (seg0 * cols + tc) * rps, WT ? (uint32_t)(kTileCols * rps) : 0u);
 #pragma unroll 4
-    for (int pass = 0; pass < kTileCols / 32; ++pass) {
-      const int col = pass * 32 + (threadIdx.x >> 3);
-      if (col < valid_cols && slot * 16 < valid_rows) {
-        int64_t seg = seg0, off = off0 + slot * 16;
-        while (off >= rps) {
-          off -= rps;
-          ++seg;
+      for (int pass = 0; pass < kTileCols / 32; ++pass) {
+        const int col = pass * 32 + (threadIdx.x >> 3);
+        if (col < valid_cols && slot * 16 < valid_rows) {
+          const uint4 w = st.q1[q1_slot(col, slot)];
+          if constexpr (WT) {
+            store_line_wt(q1rs, (uint32_t)(col * rps + off0 + slot * 16), w);
+          } else {
+            int64_t seg = seg0, off = off0 + slot * 16;
+            while (off >= rps) {
+              off -= rps;
+              ++seg;
+            }
+            store_line_nt(a.q1 + (seg * cols + tc + col) * rps + off, w);
+          }
         }
-        uint8_t* dst = a.q1 + (seg * cols + tc + col) * rps + off;
-        store_line_nt(dst, st.q1[q1_slot(col, slot)]);
       }
-    }
+    };
+    if (wt)
+      put_codes(std::true_type{});
+    else
+      put_codes(std::false_type{});
     if constexpr (BLK) {
       // Two blocked tiles of the segment's dim1 scale matrix: matrix rows
       // (x columns) tc .. tc + 255, scale column block off0 / 128 (the host
@@ -644,7 +686,14 @@ __global__ __launch_bounds__(256) void cast_kernel(CastArgs a) {
           const int64_t left = cols - (tc + 128 * t + i);   // columns from this one on
           const int valid_s = (int)min((int64_t)4, max((int64_t)0, (left + 31) / 32));
           v = mask_chunk(v, valid_s, valid_rows / 32);
-          store_line_nt(a.s1 + seg0 * a.seg_blk_bytes + (rb * a.ncb1 + off0 / 128) * 512 + i * 16, v);
+          uint8_t* pair = a.s1 + seg0 * a.seg_blk_bytes + (2 * (int64_t)ct * a.ncb1 + off0 / 128) * 512;
+          if (a.wt != 0 && (a.ncb1 + 1) * 512 < (1ll << 31)) {
+            // Tile t of the pair starts ncb1 blocked tiles after tile 0.
+            const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(pair, (uint32_t)((a.ncb1 + 1) * 512));
+            store_line_wt(rs, (uint32_t)(t * a.ncb1 * 512 + i * 16), v);
+          } else {
+            store_line_nt(pair + t * a.ncb1 * 512 + i * 16, v);
+          }
         }
       }
     } else if constexpr (KGRP) {
@@ -714,6 +763,7 @@ static CastArgs cast_args(const uint16_t* x, int64_t rows, int64_t cols, int64_t
   // the XCD running the neighbouring tiles, are slower rotated elsewhere
   // (16384 x 16384: 185 against 193 us).
   a.rotate = q0 == nullptr || blocked || (per % ct == 0 && (per / ct) % 32 == 0) ? 1u : 0u;
+  a.wt = q1 != nullptr && rows * cols <= kWriteThroughMax ? 1u : 0u;
   a.ends = nullptr;
   a.groups = 0;
   a.out_starts = nullptr;

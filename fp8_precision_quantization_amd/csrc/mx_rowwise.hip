@@ -28,6 +28,9 @@ namespace mx {
 
 constexpr int kRowThreads = 256;
 constexpr int kLoadNTRow = 2;             // cache-policy bits of the input loads: nt
+// ... of the code stores: written through (sc0 sc1); 16384 x 16384 118.5 ->
+// 116.0 us against ordinary stores, 125.3 us non-temporal (MI355X).
+constexpr int kStoreWTRow = 17;
 
 template <int WPR, int K>
 __global__ __launch_bounds__(kRowThreads) void rowwise_kernel(const uint16_t* __restrict__ x, int64_t rows,
@@ -74,13 +77,13 @@ __global__ __launch_bounds__(kRowThreads) void rowwise_kernel(const uint16_t* __
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       const uint2 c = quant8<true>(d[k], p);
-      __builtin_amdgcn_raw_buffer_store_b64((u32x2){c.x, c.y}, qs, lane * 8, (k * WPR + wr) * 512, 0);
+      __builtin_amdgcn_raw_buffer_store_b64((u32x2){c.x, c.y}, qs, lane * 8, (k * WPR + wr) * 512, kStoreWTRow);
     }
   } else {
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       const uint2 c = quant8<false>(d[k], p);
-      __builtin_amdgcn_raw_buffer_store_b64((u32x2){c.x, c.y}, qs, lane * 8, (k * WPR + wr) * 512, 0);
+      __builtin_amdgcn_raw_buffer_store_b64((u32x2){c.x, c.y}, qs, lane * 8, (k * WPR + wr) * 512, kStoreWTRow);
     }
   }
 }

@@ -41,6 +41,10 @@ constexpr int kTwCastUnroll = 4;                   // chunks per thread, step 3
 constexpr int64_t kTwElemsPerSpan = 32768;         // smallest span of step 1, in elements
 constexpr int64_t kTwMaxSpans = 2048;
 constexpr int kTwLoadNT = 2;                       // cache-policy bits of the loads of x: nt
+// ... of the code stores of step 3: written through (sc0 sc1); 16384 x 16384
+// 197.2 -> 191.2 us for the three steps against ordinary stores, 202.8 us
+// non-temporal (MI355X).
+constexpr int kTwStoreWT = 17;
 constexpr int64_t kTwScalarPerGroup = 4096;        // elements per step-3 workgroup, unaligned path
 
 struct TwPlan {
@@ -165,7 +169,7 @@ __device__ __forceinline__ void tw_cast_chunks(const u32x4 (&d)[kTwCastUnroll], 
 #pragma unroll
   for (int u = 0; u < kTwCastUnroll; ++u) {
     const uint2 c = quant8<FAST>(make_uint4(d[u][0], d[u][1], d[u][2], d[u][3]), p);
-    __builtin_amdgcn_raw_buffer_store_b64((u32x2){c.x, c.y}, qs, threadIdx.x * 8, u * kTwThreads * 8, 0);
+    __builtin_amdgcn_raw_buffer_store_b64((u32x2){c.x, c.y}, qs, threadIdx.x * 8, u * kTwThreads * 8, kTwStoreWT);
   }
 }
 
