@@ -76,18 +76,20 @@ mx_status mx_cast_dim0_dim1(const void* x, int64_t rows, int64_t cols, uint8_t* 
     return MX_ERR_SHAPE;
   if (!aligned(x, 16) || (d0 && !aligned(q_row, 8)) || (d1 && !aligned(q_col, 16)))
     return MX_ERR_ALIGN;
-  // On large, tall inputs whose 128-row scale bands all fit one workgroup's
+  // On some large inputs whose 128-row scale bands all fit one workgroup's
   // LDS, the scales are written in the blocked layout, whose stores are whole
   // lines, and then turned into the plain one in place (the same bytes).
   // Timed on MI355X against the direct kernel's partial 1- and 4-byte scale
-  // runs (both directions, 150 calls after 40): 16384 x 16384 170 against
-  // 181 us, 16384 x 4096 52 against 61, 16384 x 8192 and 8192 x 16384 91
-  // against 92, 32768 x 8192 174 against 187, 32768 x 16384 421 against 438;
-  // slower at 16640 x 5120 (68 against 61), 32768 x 4096 (98 against 92),
-  // 4096 x 16384, 8192 x 8192 and every smaller input (the conversion's own
-  // ~5-8 us and second launch), hence the bounds.
-  const bool big = (rows >= 16384 && cols >= 8192) || (rows == 16384 && cols >= 4096);
-  const bool via_blocked = big && rows % 128 == 0 && cols % 128 == 0 &&
+  // runs (both directions, 150 calls after 40, us via blocked / direct):
+  // 16384 x 16384 169.0 / 182.7, 16384 x 4096 49.8 / 58.4, 32768 x 8192
+  // 175.2 / 190.6, 32768 x 16384 421 / 438, 16384 x 8192 91.6 / 92.0; the
+  // direct kernel wins at 16384 x 5120 (56.8 / 60.7), 16640 x 8192 (89.7 /
+  // 95.5), 32768 x 4096 (88.2 / 93.4), 16640 x 5120, 12288 x 8192,
+  // 8192 x 16384, 4096 x 16384 and smaller inputs.  The direct kernel is at
+  // its slowest where both sizes are powers of two (its partial scale lines
+  // then collide), hence the rule.  Every band is then whole 16-byte chunks.
+  const bool big = (rows % 16384 == 0 && cols % 8192 == 0) || (rows == 16384 && cols == 4096);
+  const bool via_blocked = big &&
                            (!d0 || (cols / MX_BLOCK <= mx::kUnblockMaxCols && aligned(s_row, 16))) &&
                            (!d1 || (rows / MX_BLOCK <= mx::kUnblockMaxCols && aligned(s_col, 16)));
   if (via_blocked) {

@@ -323,27 +323,26 @@ hipError_t launch_blocked_grouped(const uint8_t* s, int64_t rows, int64_t cols, 
 }
 
 // The inverse map, in place: e8m0 scale matrices of R x C bytes (R % 128 ==
-// 0, C % 4 == 0, C <= kUnblockMaxCols) from the 128x4 blocked layout to the
+// 0, C % 16 == 0, C <= kUnblockMaxCols) from the 128x4 blocked layout to the
 // plain row-major one.  A 128-row band occupies the same 128 * C bytes in
 // both layouts (in the blocked one as its C / 4 tiles, one after another), so
 // one workgroup per band reads the whole band with contiguous 16-byte loads,
-// regroups it in LDS and writes it back as contiguous rows, in 16-byte
-// chunks when a row is whole chunks (1.2 us less than dword stores at 16384
-// x 16384, where both 16384 x 512 matrices go through it).  The band loads
-// are non-temporal: the cast has just written the band with non-temporal
-// stores, and cached loads of it took ~4 us longer at 16384 x 16384 (172 ->
-// 168 us for the whole plain-scale call), although a kernel that reads the
-// plain scales right after then takes longer (the two layout launches of
-// both 16384 x 512 matrices ~5 us more); the whole-line 16-byte stores are
-// non-temporal too (0.2 us).  Dword j of chunk
-// i of tile k is row i + 32 j, scale columns 4 k .. 4 k + 3.  Every load of a
-// band has returned (its value is in LDS) before the barrier, and only after
-// it does any thread of the workgroup store into the band.
+// regroups it in LDS and writes it back as contiguous rows of 16-byte chunks.
+// Dword j of chunk i of tile k is row i + 32 j, scale columns 4 k .. 4 k + 3.
+// Every load of a band has returned (its value is in LDS) before the
+// barrier, and only after it does any thread of the workgroup store into the
+// band.
+//
+// The band loads are non-temporal: cached loads took ~4 us longer at 16384 x
+// 16384 (172 -> 168 us for the whole plain-scale call; 32768 x 8192 184 ->
+// 175 us; smaller inputs even), although a kernel that reads the plain
+// scales right after then takes longer (the two layout launches of both
+// 16384 x 512 matrices ~5 us more); the whole-line 16-byte stores are
+// non-temporal too (0.2 us).
 constexpr int kUnblockTiles = kUnblockMaxCols / 4;     // tiles per band, at most
 constexpr int kUnblockPitch = kUnblockTiles + 1;       // dwords per staged row (odd: no bank conflicts)
 constexpr int kUnblockThreads = 1024;                  // 16 waves share a band's latency
 constexpr int kUnblockChunks = kUnblockTiles * 32 / kUnblockThreads;   // 16-byte chunks per thread, at most
-constexpr int kUnblockDwords = kUnblockTiles * kTileRows / kUnblockThreads;   // dwords stored per thread, at most
 
 __global__ __launch_bounds__(kUnblockThreads) void unblock_kernel(uint8_t* m0, int64_t c0, int64_t bands0,
                                                                   uint8_t* m1, int64_t c1) {
@@ -357,18 +356,17 @@ __global__ __launch_bounds__(kUnblockThreads) void unblock_kernel(uint8_t* m0, i
     c = c1;
   }
   const int tiles = (int)(c / 4);
-  const int chunks = tiles * 32;
+  const int chunks = tiles * 32;   // 16-byte chunks of the band, in either layout
   uint8_t* base = m + band * kTileRows * c;
   const int t = threadIdx.x;
   uint4 v[kUnblockChunks];
 #pragma unroll
   for (int n = 0; n < kUnblockChunks; ++n) {
     const int q = t + kUnblockThreads * n;
-    if (q < chunks)
-      {
-        const u32x4 l = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + 16 * (int64_t)q));
-        v[n] = make_uint4(l[0], l[1], l[2], l[3]);
-      }
+    if (q < chunks) {
+      const u32x4 l = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + 16 * (int64_t)q));
+      v[n] = make_uint4(l[0], l[1], l[2], l[3]);
+    }
   }
 #pragma unroll
   for (int n = 0; n < kUnblockChunks; ++n) {
@@ -382,59 +380,35 @@ __global__ __launch_bounds__(kUnblockThreads) void unblock_kernel(uint8_t* m0, i
     }
   }
   __syncthreads();
-  // Rows of whole 16-byte chunks (tiles % 4 == 0): plain chunk e = r *
-  // (tiles / 4) + j (dwords 4 j .. 4 j + 3 of row r) for e = t, t + 1024,
-  // ...; else plain dword d = r * tiles + k for d = t, t + 1024, ...  All LDS
-  // reads first, then the stores.
-  if (tiles % 4 == 0) {
-    uint4* out = reinterpret_cast<uint4*>(base);
-    const int per_row = tiles / 4;
-    const int total = per_row * kTileRows;
-    constexpr int kChunks = kUnblockDwords / 4;
-    uint4 w[kChunks];
+  // Plain chunk e = r * (tiles / 4) + j holds dwords 4 j .. 4 j + 3 of row r,
+  // for e = t, t + 1024, ...  All LDS reads first, then the stores.
+  const int per_row = tiles / 4;
+  uint4 w[kUnblockChunks];
 #pragma unroll
-    for (int n = 0; n < kChunks; ++n) {
-      const int e = t + kUnblockThreads * n;
-      if (e < total) {
-        const int r = e / per_row, j = e - r * per_row;
-        const uint32_t* src = &staged[r * kUnblockPitch + 4 * j];
-        w[n] = make_uint4(src[0], src[1], src[2], src[3]);
-      }
-    }
-#pragma unroll
-    for (int n = 0; n < kChunks; ++n) {
-      const int e = t + kUnblockThreads * n;
-      if (e < total)
-        store_line_nt(reinterpret_cast<uint8_t*>(out + e), w[n]);
-    }
-    return;
-  }
-  uint32_t* out = reinterpret_cast<uint32_t*>(base);
-  const int total = tiles * kTileRows;
-  const int step_r = kUnblockThreads / tiles, step_k = kUnblockThreads % tiles;
-  int r = t / tiles, k = t % tiles;
-  uint32_t w[kUnblockDwords];
-#pragma unroll
-  for (int n = 0; n < kUnblockDwords; ++n) {
-    if (t + kUnblockThreads * n < total)
-      w[n] = staged[r * kUnblockPitch + k];
-    r += step_r;
-    k += step_k;
-    if (k >= tiles) {
-      k -= tiles;
-      ++r;
+  for (int n = 0; n < kUnblockChunks; ++n) {
+    const int e = t + kUnblockThreads * n;
+    if (e < chunks) {
+      const int r = e / per_row, j = e - r * per_row;
+      const uint32_t* src = &staged[r * kUnblockPitch + 4 * j];
+      w[n] = make_uint4(src[0], src[1], src[2], src[3]);
     }
   }
 #pragma unroll
-  for (int n = 0; n < kUnblockDwords; ++n) {
-    const int d = t + kUnblockThreads * n;
-    if (d < total)
-      out[d] = w[n];
+  for (int n = 0; n < kUnblockChunks; ++n) {
+    const int e = t + kUnblockThreads * n;
+    if (e < chunks)
+      store_line_nt(base + 16 * (int64_t)e, w[n]);
   }
 }
 
 hipError_t launch_unblock_inplace(uint8_t* m0, int64_t r0, int64_t c0, uint8_t* m1, int64_t r1, int64_t c1,
                                   hipStream_t stream) {
+  const auto fits = [](const uint8_t* m, int64_t r, int64_t c) {
+    return m == nullptr || (r % kTileRows == 0 && c % 16 == 0 && c > 0 && c <= kUnblockMaxCols &&
+                            ((uintptr_t)m % 16) == 0);
+  };
+  if (!fits(m0, r0, c0) || !fits(m1, r1, c1))
+    return hipErrorInvalidValue;
   const int64_t b0 = m0 != nullptr ? r0 / kTileRows : 0;
   const int64_t b1 = m1 != nullptr ? r1 / kTileRows : 0;
   if (b0 + b1 == 0)

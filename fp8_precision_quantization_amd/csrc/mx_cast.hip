@@ -32,7 +32,10 @@
 //   that size, where that is faster again (16640 x 5120 M-grouped: 63.1 ->
 //   60.8 us; at 16384 x 16384 it would be 160.6 -> 201 us): 30 shapes from
 //   4096 x 2048 to 32768 x 16384 split cleanly at that size, which is where
-//   the two code matrices stop fitting the 256 MB memory-side cache;
+//   the two code matrices stop fitting the 256 MB memory-side cache (timed
+//   on the dim0+dim1 casts; the dim1-only cast takes the same rule, and its
+//   (16, 8192, 5120) workload, 640 MiB of codes, stays non-temporal: written
+//   through it took 345 against 338 us);
 // - the dim0 row segments, whose lines neighbouring lanes complete, are
 //   written through (sc0 sc1: 16384 x 16384 161.0 -> 160.6 us, 16640 x 5120
 //   63.5 -> 63.1 us; non-temporal there cost time);

@@ -34,9 +34,9 @@ hipError_t launch_blocked_grouped(const uint8_t* s, int64_t rows, int64_t cols, 
                                   int64_t* out_starts, hipStream_t stream);
 
 // In place, blocked -> plain: scale matrices m0 (r0 x c0 bytes) and m1 (r1 x
-// c1), either may be null; rows multiples of 128, columns multiples of 4 and
-// at most kUnblockMaxCols (a 128-row band then fills 128 KiB of LDS), 16-byte
-// aligned.
+// c1), either may be null; rows multiples of 128, columns multiples of 16 (a
+// plain row is whole 16-byte chunks) and at most kUnblockMaxCols (a 128-row
+// band then fills 128 KiB of LDS), 16-byte aligned.
 constexpr int64_t kUnblockMaxCols = 1024;
 hipError_t launch_unblock_inplace(uint8_t* m0, int64_t r0, int64_t c0, uint8_t* m1, int64_t r1, int64_t c1,
                                   hipStream_t stream);

@@ -100,11 +100,12 @@ MX_API const char* mx_status_string(int status);
  * pair NULL); both pairs NULL, a half-NULL pair or x NULL -> MX_ERR_NULL.
  * rows and cols must be >= 0 and multiples of 32, cols <= 2^25, else
  * MX_ERR_SHAPE.  Outputs must not overlap the input or each other.
- * Where rows >= 16384 and cols >= 4096 are multiples of 128, each present
- * scale matrix has at most 512 columns and is 16-byte aligned, the call
- * enqueues two kernels: the cast writing the scales in the 128x4 blocked
- * layout, then their conversion to the layout above in place.  Until the second has run, the scale buffers
- * hold the blocked bytes; both are on `stream`, so stream order hides this.
+ * Where rows are a multiple of 16384 and cols of 8192 (or the shape is
+ * 16384 x 4096), each present scale matrix has at most 1024 columns and is
+ * 16-byte aligned, the call enqueues two kernels: the cast writing the
+ * scales in the 128x4 blocked layout, then their conversion to the layout
+ * above in place.  Until the second has run, the scale buffers hold the
+ * blocked bytes; both are on `stream`, so stream order hides this.
  */
 MX_API mx_status mx_cast_dim0_dim1(const void* x, int64_t rows, int64_t cols,
                             uint8_t* q_row, uint8_t* s_row,

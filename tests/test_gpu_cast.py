@@ -71,17 +71,14 @@ def test_single_direction(oracle_mod, dim0, dim1):
     check_cast(oracle_mod, bits, dev, "single", dim0=dim0, dim1=dim1)
 
 
-# At least 16384 rows and 8192 cols (or exactly 16384 rows and at least
-# 4096 cols), multiples of 128, at most 1024 scale columns in each scale
-# matrix present: the scales are written in the blocked layout and converted
-# back to rows in place, one 128-row band per workgroup (16384 x 16384 is
-# covered by the full-size configuration test).  16512 x 4096 is under the
-# size bound (direct path), as are 3968 columns at 16384 rows; 4224 columns
-# give 33 blocked tiles per 128-row band of the row scales, which the
-# in-place conversion writes back as dwords (whole 16-byte chunks need a
-# multiple of 4 tiles); 16640 x 8192 has 520-column dim1 scales (130 tiles
-# per band, past 512 columns, written back as dwords).
-VIA_BLOCKED = [(16384, 4096), (16512, 4096), (16384, 3968), (16384, 4224), (16640, 8192)]
+# Rows a multiple of 16384 and cols a multiple of 8192, or exactly 16384 x
+# 4096, at most 1024 scale columns in each scale matrix present: the scales
+# are written in the blocked layout and converted back to rows in place, one
+# 128-row band per workgroup (16384 x 16384 is covered by the full-size
+# configuration test, 32768 x 8192 below).  16384 x 4096 and 16384 x 8192
+# take that path; 16512 x 4096, 16384 x 3968, 16384 x 4224 and 16384 x 5120
+# sit next to it and take the direct kernel.
+VIA_BLOCKED = [(16384, 4096), (16384, 8192), (16512, 4096), (16384, 3968), (16384, 4224), (16384, 5120)]
 
 
 @pytest.mark.parametrize("dim0,dim1", [(True, True), (True, False), (False, True)])
