@@ -110,11 +110,44 @@ def blocked_bytes(rows, cols, batch=1):
     return batch * (rows * cols + pad(rows, 128) * pad(cols, 4))
 
 
-def sources_digest():
+def code_of(text):
+    """C/C++ source with its comments removed and each line's trailing
+    blanks dropped, empty lines skipped: what the compiler sees, so that a
+    change to a comment leaves the digest as it was."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        ch = text[i]
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif ch in "\"'":
+            j = i + 1
+            while j < n and text[j] != ch:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(ch)
+            i += 1
+    lines = ("".join(out)).split("\n")
+    return "\n".join(l.rstrip() for l in lines if l.strip())
+
+
+def sources_digest(read=None):
+    """First 16 hex digits of sha256 over the code (comments stripped) of the
+    cast kernel's sources, in order; read(path) -> text, default the files."""
     h = hashlib.sha256()
     for p in CAST_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        if read is None:
+            with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+                text = f.read()
+        else:
+            text = read(p)
+        h.update(code_of(text).encode("utf-8"))
     return h.hexdigest()[:16]
 
 
