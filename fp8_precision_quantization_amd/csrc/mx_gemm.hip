@@ -67,6 +67,7 @@ namespace mx {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kGemmThreads = 256;
 constexpr int kGemmTile = 256;                 // rows and columns of C per workgroup
@@ -104,7 +105,16 @@ __device__ __forceinline__ int32_t wave_sum(int32_t v) {
   return v;
 }
 
-// binary32 -> bf16 bits, nearest-even; NaN -> 0x7FC0.
+// Two binary32 values -> their bf16 bits, nearest-even, packed with the
+// first in the low half: gfx950's v_cvt_pk_bf16_f32, one instruction for
+// both.  Checked on MI355X against a software nearest-even rounding over
+// every binary32 bit pattern: identical for all non-NaN inputs (subnormal
+// results and overflow to Inf included); NaN stays NaN.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+}
+// One value, for the per-element stores of outputs whose rows are not whole
+// 16-byte chunks (the same rounding; NaN -> 0x7FC0).
 __device__ __forceinline__ uint16_t to_bf16(float f) {
   const uint32_t u = __float_as_uint(f);
   if ((u & 0x7FFFFFFFu) > 0x7F800000u)
@@ -506,12 +516,16 @@ __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
         for (int j = 0; j < kGemmWaveBlocks; ++j)
 #pragma unroll
           for (int v = 0; v < 16; v += 2) {
-            // rows R and R + 1 of column r; lanes r and r ^ 1 trade so that
-            // the even lane writes row R and the odd lane row R + 1, each as
-            // the bf16 pair of columns r & ~1 and (r & ~1) + 1
-            const uint32_t lo16 = to_bf16(acc[i][j][v]), hi16 = to_bf16(acc[i][j][v + 1]);
-            const uint32_t recv = quad_swap1(odd ? lo16 : hi16);
-            const uint32_t word = odd ? (recv | (hi16 << 16)) : (lo16 | (recv << 16));
+            // rows R and R + 1 of column r; lanes r and r ^ 1 trade both
+            // values so that the even lane writes row R and the odd lane row
+            // R + 1, each as the bf16 pair of columns r & ~1 and (r & ~1) +
+            // 1, converted in one instruction.  (Selecting which value to
+            // send instead lets the compiler turn the pair of reads into one
+            // lane-indexed read of the accumulators, a chain of 16 selects.)
+            const float a0 = acc[i][j][v], a1 = acc[i][j][v + 1];
+            const float n0 = __uint_as_float(quad_swap1(__float_as_uint(a0)));   // row R of the other lane
+            const float n1 = __uint_as_float(quad_swap1(__float_as_uint(a1)));   // row R + 1 of the other lane
+            const uint32_t word = odd ? pack_bf16(n1, a1) : pack_bf16(a0, n0);
             const int row = wm * 128 + 32 * i + 8 * (v / 4) + 4 * h + (v % 4) + (odd ? 1 : 0);
             const int d = wn * 64 + 16 * j + (r >> 1);
             ldsw[row * 128 + (d ^ swz(row))] = word;
