@@ -114,7 +114,12 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 // One value, for the per-element stores of outputs whose rows are not whole
-// 16-byte chunks (the same rounding; NaN -> 0x7FC0).
+// 16-byte chunks (the same rounding; NaN -> 0x7FC0).  With this path the
+// bf16 kernels keep 12 accumulators in scratch between the main loop and the
+// epilogue (12 dword stores per lane and tile, reloaded only on this path);
+// converting this path in pairs with pack_bf16 as well removes them but
+// changes the register allocation of the main loop, which then ran 8%
+// slower (dense 611 -> 662 us).
 __device__ __forceinline__ uint16_t to_bf16(float f) {
   const uint32_t u = __float_as_uint(f);
   if ((u & 0x7FFFFFFFu) > 0x7F800000u)
@@ -501,34 +506,41 @@ __global__ __launch_bounds__(kGemmThreads) void mx_gemm_kernel(GemmArgs a) {
   // the registers it would take 2-byte stores, 1024 instructions per
   // workgroup, and measured a fifth of the GEMM's time.  In LDS, dword d of
   // row R (columns 2 d, 2 d + 1) sits at d ^ swz(R), swz(R) = 16 (2 ((R >> 2)
-  // & 1) + (R & 1)): the four rows one write instruction touches (R, R + 1,
-  // R + 4, R + 5) land on different 16-bank groups, and a 16-byte chunk
+  // & 1) + (R & 1)): the two rows one write instruction touches (R and R + 4,
+  // 16 dwords each) land on different 16-bank groups, and a 16-byte chunk
   // stays whole.
   if constexpr (BF16) {
     if ((a.n & 7) == 0 && (reinterpret_cast<uintptr_t>(c) & 15) == 0) {
       uint32_t* ldsw = reinterpret_cast<uint32_t*>(&lds[0][0][0]);
       auto swz = [](int row) { return 16 * (2 * ((row >> 2) & 1) + (row & 1)); };
       lds_barrier();   // every wave is done reading operands from LDS
-      const bool odd = (r & 1) != 0;
+      // Rows R and R + 1 of column r (accumulators v and v + 1) are converted
+      // together and written as the two 2-byte halves of their dwords (the
+      // lanes of columns r and r ^ 1 fill one dword).  With R = wm 128 + 32 i
+      // + 8 (v / 4) + 4 h + v % 4 (v even), bit 2 of R is h and bit 0 is 0,
+      // so swz(R) = 32 h and swz(R + 1) = 32 h + 16: the byte address of
+      // column r of row R is 4 (128 R + wn 64 + 16 (j ^ 2 h) + r / 2) + 2 (r &
+      // 1), a per-lane base for each j plus a constant.  (Trading values
+      // with the neighbouring lane so that each lane writes whole dwords cost
+      // more VALU time than the second LDS write: dense 609 against 599 us.)
+      uint8_t* ldsb = &lds[0][0][0];
+      const int lane_b = 512 * (wm * 128 + 4 * h) + 4 * (wn * 64 + (r >> 1)) + 2 * (r & 1);
+      int base_r[kGemmWaveBlocks], base_r1[kGemmWaveBlocks];
+#pragma unroll
+      for (int j = 0; j < kGemmWaveBlocks; ++j) {
+        base_r[j] = lane_b + 64 * (j ^ (2 * h));
+        base_r1[j] = lane_b + 512 + 64 * (j ^ (2 * h) ^ 1);
+      }
 #pragma unroll
       for (int i = 0; i < kGemmWaveBlocks; ++i)
 #pragma unroll
         for (int j = 0; j < kGemmWaveBlocks; ++j)
 #pragma unroll
           for (int v = 0; v < 16; v += 2) {
-            // rows R and R + 1 of column r; lanes r and r ^ 1 trade both
-            // values so that the even lane writes row R and the odd lane row
-            // R + 1, each as the bf16 pair of columns r & ~1 and (r & ~1) +
-            // 1, converted in one instruction.  (Selecting which value to
-            // send instead lets the compiler turn the pair of reads into one
-            // lane-indexed read of the accumulators, a chain of 16 selects.)
-            const float a0 = acc[i][j][v], a1 = acc[i][j][v + 1];
-            const float n0 = __uint_as_float(quad_swap1(__float_as_uint(a0)));   // row R of the other lane
-            const float n1 = __uint_as_float(quad_swap1(__float_as_uint(a1)));   // row R + 1 of the other lane
-            const uint32_t word = odd ? pack_bf16(n1, a1) : pack_bf16(a0, n0);
-            const int row = wm * 128 + 32 * i + 8 * (v / 4) + 4 * h + (v % 4) + (odd ? 1 : 0);
-            const int d = wn * 64 + 16 * j + (r >> 1);
-            ldsw[row * 128 + (d ^ swz(row))] = word;
+            const uint32_t pair = pack_bf16(acc[i][j][v], acc[i][j][v + 1]);
+            const int off = 512 * (32 * i + 8 * (v / 4) + (v % 4));
+            *reinterpret_cast<uint16_t*>(ldsb + base_r[j] + off) = (uint16_t)pair;
+            *reinterpret_cast<uint16_t*>(ldsb + base_r1[j] + off) = (uint16_t)(pair >> 16);
           }
       lds_barrier();
       // thread t: 16-byte chunk t % 32 of rows t / 32 + 8 p
